@@ -1,0 +1,74 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail a pin: evidence
+that the pins constrain the oracle and do not merely restate it."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests import test_oracle_expcast as TE
+from tests import test_oracle_attention as TA
+
+
+def test_flipped_beta_fails_the_agreement_pin(monkeypatch):
+    monkeypatch.setattr(O, "EXPCAST_OFFSET", np.float32(56.35))
+    with pytest.raises(AssertionError):
+        TE.test_agreement_per_doubling_is_79_6_percent()
+
+
+def test_wrong_code_offset_fails_the_p_equals_one_pin(monkeypatch):
+    monkeypatch.setattr(O, "EXPCAST_OFFSET", np.float32(47.65))   # as if the exponent bias were 6
+    with pytest.raises(AssertionError):
+        TE.test_probability_one_is_the_e4m3_byte_of_one()
+
+
+def test_dropped_mean_restore_fails_the_softmax_pin(monkeypatch):
+    real = O.online_attention
+
+    def no_restore(Qd, Kd, Vres, means, *a, **k):
+        return real(Qd, Kd, Vres, np.zeros_like(means), *a, **k)
+
+    monkeypatch.setattr(O, "online_attention", no_restore)
+    with pytest.raises(AssertionError):
+        TA.test_online_softmax_with_mean_restore_is_exact_softmax(300)
+
+
+def test_ties_away_from_zero_fail_the_e4m3_pin(monkeypatch):
+    real_rint = np.rint
+
+    def round_half_away(x):
+        return np.sign(x) * np.floor(np.abs(x) + 0.5)
+
+    monkeypatch.setattr(O.np, "rint", round_half_away)
+    x = np.float32([1.0625, 1.1875, 3 * 2 ** -11])          # exact ties of E4M3
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(x)
+    monkeypatch.setattr(O.np, "rint", real_rint)
+    assert (got != want).any()
+
+
+def test_missing_running_max_rescale_fails_the_softmax_pin(monkeypatch):
+    real_exp2 = np.exp2
+    calls = {"n": 0}
+
+    def stale_alpha(x, *a, **k):
+        return real_exp2(x, *a, **k)
+
+    src = O.online_attention
+
+    def no_rescale(Qd, Kd, Vres, means, N, sq, ks, c0, p_mode, rows, record=None):
+        # run block by block but never rescale the accumulators
+        nb = O.n_blocks(N)
+        q = Qd[rows]
+        U = 0
+        l = 0
+        for t in range(nb):
+            k0, k1 = t * 128, min(N, (t + 1) * 128)
+            x = q @ Kd[k0:k1].T * float(c0)
+            P = np.exp2(x - x.max(1, keepdims=True))
+            l = l + P.sum(1)
+            U = U + P @ Vres[k0:k1] + P.sum(1)[:, None] * means[t][None]
+        return U / l[:, None]
+
+    monkeypatch.setattr(O, "online_attention", no_rescale)
+    with pytest.raises(AssertionError):
+        TA.test_online_softmax_with_mean_restore_is_exact_softmax(300)
