@@ -1,0 +1,343 @@
+// Non-causal FP8 flash attention with V-Smooth mean restore and ExpCast-FP8,
+// hand-written for gfx950 (MI355X).
+//
+// Method: paper digest "VC-Attention: Value Smoothing and Softmax Casting for
+// Low-bit Attention", V-Smooth paragraph (the residual is quantised and each
+// block mean is added back with one outer product of the row sums online
+// softmax already keeps, without a second pass over V) and ExpCast-FP8 paragraph
+// (the P byte is an affine function of the log-domain score: one fused
+// multiply-add, round to nearest even, clip to the normal range, beta = -0.35).
+// News article "Nunchux open-sources VC-Attention", sections "V-Smooth" (item
+// Restore) and "ExpCast-FP8".
+//
+// Design (MI355X-first, not the pages' Blackwell kernel):
+//  * one workgroup = 4 wavefronts = one 128-query block (one Q scale); every
+//    wavefront owns 32 queries and runs V_MFMA_F32_32X32X64_F8F6F4 (OCP E4M3).
+//  * scores are computed transposed, S^T = K . Q^T (K rows are the MFMA rows),
+//    so each lane holds the scores of ONE query.  Row max needs one cross-lane
+//    step, and the ExpCast bytes land directly in the lane layout of the
+//    B operand of O^T = V^T . P^T: no shuffle of P.  The K rows of a tile are fed
+//    to the MFMA in the order sigma() so that every lane's P bytes are 32
+//    consecutive keys, matching 32 consecutive bytes of the transposed V block.
+//  * K and V^T tiles (16 KiB each) are double-buffered in LDS with an XOR chunk
+//    swizzle that keeps the 128-bit operand reads free of bank conflicts.
+//  * the row sum of the decoded P bytes comes from one extra MFMA against an
+//    all-ones operand (exact: every E4M3 value is a multiple of 2^-9), and the
+//    block mean is restored as U += rowsum (x) mean_t / sv with fp32 FMAs.
+//  * workgroups are ordered head-major and handed to the 8 XCDs in contiguous
+//    ranges, so the workgroups sharing an XCD's L2 stream the same K/V blocks.
+#include "attn_common.h"
+
+namespace vc {
+
+constexpr int kAttnThreads = 256;
+constexpr int kTile = kBlock * kD;   // bytes of one K or V^T tile
+
+struct AttnArgs {
+  const uint8_t* q;  const float* qs;
+  const uint8_t* k;  const float* ks;
+  const uint8_t* v;  const float* vs;
+  const uint16_t* means;
+  float* out;
+  float* sdump; uint8_t* pdump;
+  int N, nb, BH;
+  float c0;
+};
+
+template <int kPMode, bool kDump>
+__global__ void __launch_bounds__(kAttnThreads) attn_fp8_e4m3(AttnArgs a) {
+  __shared__ __align__(16) uint8_t Ks[2][kTile];
+  __shared__ __align__(16) uint8_t Vs[2][kTile];
+  __shared__ __align__(16) float Mu[2][kD];
+  __shared__ float InvSv[kD];
+  __shared__ float Sv[kD];
+
+  const int nqb = a.nb;
+  const int item = xcd_item(blockIdx.x, nqb * a.BH);
+  const int bh = item / nqb, qb = item % nqb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, col = lane & 31;
+  const int N = a.N, nb = a.nb;
+  const long long Np = (long long)nb * kBlock;
+
+  if (tid < kD) {
+    const float sv = a.vs[(long long)bh * kD + tid];
+    const float svp = sv > 0.0f ? sv : 1.0f;   // an all-zero residual channel keeps its mean
+    Sv[tid] = svp;
+    InvSv[tid] = 1.0f / svp;
+  }
+
+  // Q operand (B of S^T = K.Q^T): query row, 32 bytes per channel half.
+  const int qrow = qb * kBlock + wave * 32 + col;
+  v8i qop[2];
+  {
+    const uint8_t* qp = a.q + ((long long)bh * Np + qrow) * kD;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(qp + 64 * c2 + 32 * g);
+      const uint4 hi = *reinterpret_cast<const uint4*>(qp + 64 * c2 + 32 * g + 16);
+      qop[c2][0] = lo.x; qop[c2][1] = lo.y; qop[c2][2] = lo.z; qop[c2][3] = lo.w;
+      qop[c2][4] = hi.x; qop[c2][5] = hi.y; qop[c2][6] = hi.z; qop[c2][7] = hi.w;
+    }
+  }
+  const float sq = a.qs[(long long)bh * nb + qb];
+
+  const uint8_t* kbase = a.k + (long long)bh * Np * kD;
+  const uint8_t* vbase = a.v + (long long)bh * nb * kTile;
+  const uint16_t* mbase = a.means + (long long)bh * nb * kD;
+
+  // K and V^T tiles go global -> LDS directly.  Instruction j (16 per tile,
+  // 4 per wave) fills LDS bytes [1024j, 1024j+1024): lane i writes row
+  // 8j + i/8 at chunk position i%8, so it fetches the global chunk that the
+  // XOR swizzle puts there.
+  uint32_t mr = 0;
+  auto load_tile = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * i + wave;
+      const int row = 8 * j + (lane >> 3), pos = lane & 7;
+      dma16(kbase + (long long)t * kTile + row * kD + 16 * (pos ^ swz_k(row)), &Ks[buf][1024 * j]);
+      dma16(vbase + (long long)t * kTile + row * kD + 16 * (pos ^ swz_v(row)), &Vs[buf][1024 * j]);
+    }
+    if (tid < kD) mr = mbase[(long long)t * kD + tid];
+  };
+  auto store_means = [&](int buf) {
+    if (tid < kD) Mu[buf][tid] = bf16_bits_to_f32(mr) * InvSv[tid];
+  };
+
+  load_tile(0, 0);
+  __syncthreads();          // InvSv ready
+  store_means(0);
+  wait_dma();
+  __syncthreads();
+
+  v16f o[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
+  float mx = -__builtin_inff();
+  float l = 0.0f;
+  v8i ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0
+
+  for (int t = 0; t < nb; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nb) load_tile(t + 1, buf ^ 1);
+
+    // ---- S^T = K_t . Q^T : 4 blocks of 32 keys x 32 queries ----
+    v16f s[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[m][r] = 0.0f;
+      const int row = sigma(m, col);
+      const uint8_t* rb = &Ks[buf][row * kD];
+      const int sw = swz_k(row);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) s[m] = mfma32(lds_op(rb, 4 * c2 + 2 * g, sw), qop[c2], s[m]);
+    }
+    // keys beyond N (last tile only) take no part
+    if ((t + 1) * kBlock > N) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 64 * (m >> 1) + 32 * g + 16 * (m & 1) + r;
+          if (t * kBlock + key >= N) s[m][r] = -__builtin_inff();
+        }
+    }
+    // ---- running max (log2 units) ----
+    float M = s[0][0];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) M = fmaxf(M, s[m][r]);
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float kap = (sq * a.ks[(long long)bh * nb + t]) * a.c0;
+    const float mx_new = fmaxf(mx, M * kap);
+
+    // ---- P bytes, laid out as the B operand of the P.V MFMA ----
+    uint32_t pk[16];
+    if (kPMode == VC_P_EXPCAST) {
+      const float A = 8.0f * kap;
+      const float Bc = 55.65f - 8.0f * mx_new;
+      // codes never exceed 56 unless rounding of a huge running max pushes the
+      // row maximum past 56.5; then clamp (the oracle clamps at 56 as well)
+      const bool clamp = __any(__builtin_fmaf(M, A, Bc) >= 56.5f);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          uint32_t w = 0u;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            float cf = __builtin_fmaf(s[m][4 * r4 + b], A, Bc);
+            if (clamp) cf = fminf(cf, 56.0f);
+            w = __builtin_amdgcn_cvt_pk_u8_f32(cf, b, w);   // round to nearest even, clamp [0,255]
+          }
+          // flush codes 1..7 (below the E4M3 normal range) to 0, four bytes at a time
+          const uint32_t keep = (w + 0x78787878u) & 0x80808080u;
+          w &= (keep >> 1) - (keep >> 7);
+          pk[4 * m + r4] = w;
+        }
+    } else {   // VC_P_FP32EXP_E4M3: conventional exp2 then E4M3 conversion
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float p[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) p[b] = __builtin_amdgcn_exp2f(s[m][4 * r4 + b] * kap - mx_new);
+          pk[4 * m + r4] = __builtin_amdgcn_cvt_pk_fp8_f32(
+              p[2], p[3], __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0u, false), true);
+        }
+    }
+
+    if (kDump && qrow < N) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 64 * (m >> 1) + 32 * g + 16 * (m & 1) + r;
+          const long long idx = ((long long)bh * N + qrow) * Np + (long long)t * kBlock + key;
+          const bool valid = t * kBlock + key < N;
+          a.sdump[idx] = valid ? s[m][r] : 0.0f;
+          a.pdump[idx] = (uint8_t)(valid ? (pk[4 * m + (r >> 2)] >> (8 * (r & 3))) & 0xFFu : 0u);
+        }
+    }
+
+    // ---- rescale the accumulators when the running max moved ----
+    const float alpha = __builtin_amdgcn_exp2f(mx - mx_new);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+    }
+    l *= alpha;
+    mx = mx_new;
+
+    // ---- O^T += V^T_t . P^T ; row sums from an all-ones operand ----
+    v16f rs;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rs[r] = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v8i pop;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pop[i] = (int)pk[8 * h + i];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int ch = 32 * cb + col;
+        o[cb] = mfma32(lds_op(&Vs[buf][ch * kD], 4 * h + 2 * g, swz_v(ch)), pop, o[cb]);
+      }
+      rs = mfma32(ones, pop, rs);
+    }
+    const float rsum = rs[0];
+    l += rsum;
+    // ---- mean restore: U += rowsum (x) mean_t / sv ----
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 mu = *reinterpret_cast<const float4*>(&Mu[buf][32 * cb + 8 * a4 + 4 * g]);
+        o[cb][4 * a4 + 0] = __builtin_fmaf(rsum, mu.x, o[cb][4 * a4 + 0]);
+        o[cb][4 * a4 + 1] = __builtin_fmaf(rsum, mu.y, o[cb][4 * a4 + 1]);
+        o[cb][4 * a4 + 2] = __builtin_fmaf(rsum, mu.z, o[cb][4 * a4 + 2]);
+        o[cb][4 * a4 + 3] = __builtin_fmaf(rsum, mu.w, o[cb][4 * a4 + 3]);
+      }
+
+    if (t + 1 < nb) store_means(buf ^ 1);
+    wait_dma();
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = sv * U / l, original query order ----
+  if (qrow < N) {
+    const float invl = 1.0f / l;
+    float* op = a.out + ((long long)bh * N + qrow) * kD;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int c0 = 32 * cb + 8 * a4 + 4 * g;
+        float4 val;
+        val.x = o[cb][4 * a4 + 0] * Sv[c0 + 0] * invl;
+        val.y = o[cb][4 * a4 + 1] * Sv[c0 + 1] * invl;
+        val.z = o[cb][4 * a4 + 2] * Sv[c0 + 2] * invl;
+        val.w = o[cb][4 * a4 + 3] * Sv[c0 + 3] * invl;
+        *reinterpret_cast<float4*>(op + c0) = val;
+      }
+  }
+}
+
+static int launch_e4m3(const AttnArgs& a, int p_mode, bool dump, hipStream_t st) {
+  const dim3 grid((unsigned)(a.nb * a.BH));
+  const dim3 block(kAttnThreads);
+  if (p_mode == VC_P_EXPCAST) {
+    if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, false>), grid, block, 0, st, a);
+  } else {
+    if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, false>), grid, block, 0, st, a);
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? VC_OK : vc_set_hip_error((int)e);
+}
+
+float score_scale_c0(float softmax_scale) {  // c0 = fp32(scale * log2 e)
+  return (float)((double)softmax_scale * 1.4426950408889634);
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+int vc_attn_nvfp4_launch(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
+                         const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                         const uint8_t* v_group_scales, const uint16_t* v_means, int B, int H, int N,
+                         float c0, float* out, hipStream_t st);
+
+extern "C" int vc_attn_fp8_fwd(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
+                               const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                               const uint8_t* v_group_scales, const uint16_t* v_means, int B, int H, int N,
+                               int d, float softmax_scale, int p_mode, int v_format, float* out,
+                               void* stream) {
+  if (d != kD) return VC_ERR_UNSUPPORTED;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !v_means || !out)
+    return VC_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
+  const int nb = (N + kBlock - 1) / kBlock;
+  if ((long long)nb * B * H > 0x7FFFFFFFLL) return VC_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float c0 = score_scale_c0(softmax_scale);
+  if (v_format == VC_V_E4M3 && (p_mode == VC_P_EXPCAST || p_mode == VC_P_FP32EXP_E4M3)) {
+    AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means, out, nullptr, nullptr,
+               N, nb, B * H, c0};
+    return launch_e4m3(a, p_mode, false, st);
+  }
+  if (v_format == VC_V_NVFP4 && p_mode == VC_P_FP32_BF16) {
+    if (!v_group_scales) return VC_ERR_INVALID_ARG;
+    return vc_attn_nvfp4_launch(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales,
+                                v_means, B, H, N, c0, out, st);
+  }
+  return VC_ERR_UNSUPPORTED;
+}
+
+extern "C" int vc_attn_fp8_fwd_dump(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
+                                    const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                                    const uint16_t* v_means, int B, int H, int N, int d, float softmax_scale,
+                                    int p_mode, float* out, float* s_dump, uint8_t* p_dump, void* stream) {
+  if (d != kD) return VC_ERR_UNSUPPORTED;
+  if (p_mode != VC_P_EXPCAST && p_mode != VC_P_FP32EXP_E4M3) return VC_ERR_UNSUPPORTED;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !v_means || !out || !s_dump ||
+      !p_dump)
+    return VC_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
+  const int nb = (N + kBlock - 1) / kBlock;
+  AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means, out, s_dump, p_dump,
+             N, nb, B * H, score_scale_c0(softmax_scale)};
+  return launch_e4m3(a, p_mode, true, static_cast<hipStream_t>(stream));
+}

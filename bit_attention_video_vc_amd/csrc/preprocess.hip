@@ -1,0 +1,260 @@
+// Fused gather + block mean + quantisation on gfx950.
+//
+// Method: paper digest "VC-Attention: Value Smoothing and Softmax Casting for
+// Low-bit Attention", V-Smooth paragraph (each 128-row hardware block subtracts
+// its mean, only the residual is quantised: per-channel E4M3 on the 8-bit path,
+// NVFP4 on the 4-bit path; the mean is a 16-bit vector) and preprocessing
+// paragraph (mean, gather and quantisation run fused and no high-precision
+// intermediate goes back to memory).  News article "Nunchux open-sources
+// VC-Attention", section "V-Smooth", item Demean.
+//
+// The per-channel V scale needs the amax of the residual over all N tokens of a
+// (batch, head), so the work is two HBM-streaming passes:
+//   pass 1 (one workgroup per permuted 128-row block): gather V rows, block mean
+//          (fp32 sum in row order, divided by the row count, bf16 RNE), residual
+//          amax per channel -> atomic max (E4M3) or per head (NVFP4)
+//   pass 2 (one workgroup per block): gather K and V again, K per-block E4M3,
+//          V residual codes (E4M3 with the per-channel scale, or NVFP4), Q
+//          per-block E4M3 in original order.  V codes are written transposed
+//          per block (channel-major), the operand order of the attention kernel.
+// A small clear kernel zeroes the amax accumulators first (no memset on the
+// stream, so the sequence can be captured in a graph).
+#include "vc_common.h"
+
+namespace vc {
+
+constexpr int kRowChunks = kD * 2 / 16;   // 16-byte chunks per bf16 row (16)
+
+// Stage rows of a bf16 [*, 128] tensor into LDS (row r <- src row idx[r]); rows
+// >= n are zero.  Every thread moves 16-byte chunks.
+__device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* __restrict__ src,
+                                           const int32_t* rows, int n, int nthreads) {
+  for (int q = threadIdx.x; q < kBlock * kRowChunks; q += nthreads) {
+    const int r = q / kRowChunks, ch = q % kRowChunks;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < n) v = *reinterpret_cast<const uint4*>(src + (long long)rows[r] * kD + ch * 8);
+    *reinterpret_cast<uint4*>(lds + r * kD + ch * 8) = v;
+  }
+}
+
+__global__ void clear_f32(float* p, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// Pass 1: block means and residual amax.  One thread per channel.
+template <int kVFmt>
+__global__ void __launch_bounds__(kD) pre_pass1(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                int N, int nb, uint16_t* __restrict__ means,
+                                                float* __restrict__ amax) {
+  __shared__ __align__(16) uint16_t tile[kBlock * kD];
+  __shared__ int32_t rows[kBlock];
+  __shared__ float red[kD / 64];
+  const int t = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
+  const int n = min(kBlock, N - t * kBlock);
+  rows[c] = c < n ? perm[(long long)bh * N + t * kBlock + c] : 0;
+  __syncthreads();
+  stage_rows(tile, V + (long long)bh * N * kD, rows, n, kD);
+  __syncthreads();
+  float acc = 0.0f;
+  for (int r = 0; r < n; ++r) acc += bf16_bits_to_f32(tile[r * kD + c]);
+  const uint32_t mb = f32_to_bf16_rne(acc / (float)n);
+  means[((long long)bh * nb + t) * kD + c] = (uint16_t)mb;
+  const float mu = bf16_bits_to_f32(mb);
+  float am = 0.0f;
+  for (int r = 0; r < n; ++r) am = fmaxf(am, fabsf(bf16_bits_to_f32(tile[r * kD + c]) - mu));
+  if (kVFmt == VC_V_E4M3) {
+    atomic_max_nonneg(&amax[(long long)bh * kD + c], am);
+  } else {
+    for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+    if ((c & 63) == 0) red[c >> 6] = am;
+    __syncthreads();
+    if (c == 0) atomic_max_nonneg(&amax[bh], fmaxf(red[0], red[1]));
+  }
+}
+
+// Per-block E4M3 of a staged bf16 tile (Q or K): scale = amax/448.
+__device__ void encode_block_scaled(const uint16_t* tile, int n, uint8_t* __restrict__ out_rows,
+                                    float* __restrict__ scale_out, float* red) {
+  const int tid = threadIdx.x;
+  float am = 0.0f;
+  for (int q = tid; q < n * kD; q += 256) am = fmaxf(am, fabsf(bf16_bits_to_f32(tile[q])));
+  for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+  if ((tid & 63) == 0) red[tid >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = am > 0.0f ? 448.0f / am : 0.0f;
+  if (tid == 0) *scale_out = am > 0.0f ? am / 448.0f : 0.0f;
+  // 128 rows x 8 chunks of 16 codes
+  for (int q = tid; q < kBlock * 8; q += 256) {
+    const int r = q >> 3, c0 = (q & 7) * 16;
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (r < n) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf16_bits_to_f32(tile[r * kD + c0 + 4 * e + 0]) * inv;
+        const float b = bf16_bits_to_f32(tile[r * kD + c0 + 4 * e + 1]) * inv;
+        const float cc = bf16_bits_to_f32(tile[r * kD + c0 + 4 * e + 2]) * inv;
+        const float d = bf16_bits_to_f32(tile[r * kD + c0 + 4 * e + 3]) * inv;
+        w[e] = pack2_e4m3_sat<true>(cc, d, pack2_e4m3_sat<false>(a, b, 0u));
+      }
+    }
+    *reinterpret_cast<uint4*>(out_rows + (long long)r * kD + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t e2m1_rne_sat(float x) {
+  const float a = fminf(fabsf(x), 6.0f);
+  float q;
+  if (a < 2.0f) q = __builtin_rintf(a * 2.0f) * 0.5f;
+  else if (a < 4.0f) q = __builtin_rintf(a);
+  else q = __builtin_rintf(a * 0.5f) * 2.0f;
+  q = fminf(q, 6.0f);
+  uint32_t idx = q < 2.0f ? (uint32_t)(q * 2.0f) : (q < 4.0f ? 2u + (uint32_t)q : (q < 6.0f ? 6u : 7u));
+  return idx | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+template <int kVFmt>
+__global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                 const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                 int N, int nb, const float* __restrict__ amax,
+                                                 const uint16_t* __restrict__ means,
+                                                 uint8_t* __restrict__ q_codes, float* __restrict__ q_scales,
+                                                 uint8_t* __restrict__ k_codes, float* __restrict__ k_scales,
+                                                 uint8_t* __restrict__ v_codes, float* __restrict__ v_scales,
+                                                 uint8_t* __restrict__ v_gscales) {
+  __shared__ __align__(16) uint16_t tile[kBlock * kD];
+  __shared__ int32_t rows[kBlock];
+  __shared__ float red[4];
+  __shared__ float aux[kD];   // E4M3: 448/amax_c ; NVFP4 unused
+  const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int n = min(kBlock, N - t * kBlock);
+  const long long rowbase = (long long)bh * nb * kBlock + (long long)t * kBlock;  // padded row index
+  if (tid < kBlock) rows[tid] = tid < n ? perm[(long long)bh * N + t * kBlock + tid] : 0;
+  __syncthreads();
+
+  // K: gathered, per-block scale
+  stage_rows(tile, K + (long long)bh * N * kD, rows, n, 256);
+  __syncthreads();
+  encode_block_scaled(tile, n, k_codes + rowbase * kD, k_scales + (long long)bh * nb + t, red);
+
+  // V residual
+  stage_rows(tile, V + (long long)bh * N * kD, rows, n, 256);
+  __syncthreads();
+  if (kVFmt == VC_V_E4M3) {
+    if (tid < kD) {
+      const float am = amax[(long long)bh * kD + tid];
+      aux[tid] = am > 0.0f ? 448.0f / am : 0.0f;
+      if (t == 0) v_scales[(long long)bh * kD + tid] = am > 0.0f ? am / 448.0f : 0.0f;
+    }
+    __syncthreads();
+    // channel c, rows u0..u0+15 -> 16 bytes of the transposed block
+    for (int q = tid; q < kD * 8; q += 256) {
+      const int c = q >> 3, u0 = (q & 7) * 16;
+      const float mu = bf16_bits_to_f32(means[((long long)bh * nb + t) * kD + c]);
+      const float inv = aux[c];
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x[4];
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          const int u = u0 + 4 * e + z;
+          x[z] = u < n ? (bf16_bits_to_f32(tile[u * kD + c]) - mu) * inv : 0.0f;
+        }
+        w[e] = pack2_e4m3_sat<true>(x[2], x[3], pack2_e4m3_sat<false>(x[0], x[1], 0u));
+        if (u0 + 4 * e >= n) w[e] = 0u;   // padding rows are zero bytes (not -0)
+        else {
+#pragma unroll
+          for (int z = 1; z < 4; ++z)
+            if (u0 + 4 * e + z >= n) w[e] &= ~(0xFFu << (8 * z));
+        }
+      }
+      *reinterpret_cast<uint4*>(v_codes + (((long long)bh * nb + t) * kD + c) * kBlock + u0) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  } else {
+    const float St = amax[bh] / 2688.0f;             // amax_all / (6 * 448)
+    const float six_st = 6.0f * St;
+    if (t == 0 && tid == 0) v_scales[bh] = St;
+    // channel c, group of 16 rows u0..u0+15: one E4M3 group scale, 8 packed bytes
+    for (int q = tid; q < kD * 8; q += 256) {
+      const int c = q >> 3, g = q & 7, u0 = g * 16;
+      const float mu = bf16_bits_to_f32(means[((long long)bh * nb + t) * kD + c]);
+      float r[16];
+      float gam = 0.0f;
+#pragma unroll
+      for (int z = 0; z < 16; ++z) {
+        const int u = u0 + z;
+        r[z] = u < n ? bf16_bits_to_f32(tile[u * kD + c]) - mu : 0.0f;
+        if (u < n) gam = fmaxf(gam, fabsf(r[z]));
+      }
+      const uint32_t sg = St > 0.0f ? f32_to_e4m3_sat(gam / six_st) : 0u;
+      const float dsg = e4m3_to_f32(sg) * St;
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int z = 0; z < 16; ++z) {
+        const uint32_t nib = (u0 + z < n && dsg > 0.0f) ? e2m1_rne_sat(r[z] / dsg) : 0u;
+        w[z >> 3] |= nib << (4 * (z & 7));
+      }
+      *reinterpret_cast<uint2*>(v_codes + (((long long)bh * nb + t) * kD + c) * (kBlock / 2) + u0 / 2) =
+          make_uint2(w[0], w[1]);
+      v_gscales[((long long)bh * nb * 8 + t * 8 + g) * kD + c] = (uint8_t)sg;
+    }
+  }
+  __syncthreads();
+
+  // Q: original order, per-block scale
+  if (Q) {
+    if (tid < kBlock) rows[tid] = t * kBlock + tid;
+    __syncthreads();
+    stage_rows(tile, Q + (long long)bh * N * kD, rows, n, 256);
+    __syncthreads();
+    encode_block_scaled(tile, n, q_codes + rowbase * kD, q_scales + (long long)bh * nb + t, red);
+  }
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" size_t vc_preprocess_workspace(int B, int H, int N, int d, int v_format) {
+  if (B < 1 || H < 1 || N < 1 || d != kD) return 0;
+  const long long BH = (long long)B * H;
+  return v_format == VC_V_NVFP4 ? (size_t)BH * sizeof(float) : (size_t)BH * kD * sizeof(float);
+}
+
+extern "C" int vc_preprocess_quant(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                   int B, int H, int N, int d, int v_format, uint8_t* q_codes, float* q_scales,
+                                   uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
+                                   uint8_t* v_group_scales, uint16_t* v_means, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (d != kD) return VC_ERR_UNSUPPORTED;
+  if (v_format != VC_V_E4M3 && v_format != VC_V_NVFP4) return VC_ERR_UNSUPPORTED;
+  if (!K || !V || !perm || !k_codes || !k_scales || !v_codes || !v_scales || !v_means) return VC_ERR_INVALID_ARG;
+  if (Q && (!q_codes || !q_scales)) return VC_ERR_INVALID_ARG;
+  if (v_format == VC_V_NVFP4 && !v_group_scales) return VC_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1 || (long long)B * H > 65535) return VC_ERR_INVALID_ARG;
+  const size_t need = vc_preprocess_workspace(B, H, N, d, v_format);
+  if (!workspace || workspace_bytes < need) return VC_ERR_WORKSPACE;
+  const long long BH = (long long)B * H;
+  const int nb = (N + kBlock - 1) / kBlock;
+  float* amax = static_cast<float*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long na = (long long)(need / sizeof(float));
+  hipLaunchKernelGGL(clear_f32, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, st, amax, na);
+  const dim3 grid(nb, (unsigned)BH);
+  if (v_format == VC_V_E4M3) {
+    hipLaunchKernelGGL(pre_pass1<VC_V_E4M3>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
+    hipLaunchKernelGGL(pre_pass2<VC_V_E4M3>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
+                       q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales);
+  } else {
+    hipLaunchKernelGGL(pre_pass1<VC_V_NVFP4>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
+    hipLaunchKernelGGL(pre_pass2<VC_V_NVFP4>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
+                       q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return vc_set_hip_error((int)e);
+  return VC_OK;
+}

@@ -1,0 +1,323 @@
+// V-Smooth grouping on gfx950: k-means over the Value tokens of every
+// (batch, head) and a stable sort of the tokens by cluster label.
+//
+// Method: paper digest "VC-Attention: Value Smoothing and Softmax Casting for
+// Low-bit Attention", V-Smooth paragraph (online k-means per batch and head,
+// Key and Value reordered by cluster label); news article "Nunchux open-sources
+// VC-Attention", section "V-Smooth", item Group.
+//
+// The arithmetic is fixed so that labels are reproducible bit for bit:
+//   distance  dot = fmaf chain over channels 0..127, cc = same for c.c,
+//             score = fmaf(-2, dot, cc); argmin, lowest index on ties
+//   update    int64 sums of rint(v * 2^24) (order-free, so atomics are exact),
+//             centroid = (float)((double)sum * 2^-24 / (double)count)
+//
+// Kernels (all on the caller's stream, launched T times for assign/update):
+//   kmeans_init     centroid c <- V[floor(c*N/k)], zero the accumulators, |c|^2
+//   kmeans_assign   one token per lane, centroids in LDS in groups of four (one
+//                   128-bit LDS read feeds four independent FMA chains); labels;
+//                   fixed-point sums into LDS (k <= 64) then one global atomic
+//                   per non-zero partial
+//   kmeans_update   new centroids, zero the accumulators, |c|^2
+//   sort_hist / sort_scan / sort_scatter   stable counting sort by label
+#include "vc_common.h"
+
+namespace vc {
+
+constexpr int kAssignThreads = 512;
+constexpr int kTokPerThread = 2;
+constexpr int kTokPerWG = kAssignThreads * kTokPerThread;  // 1024 tokens
+constexpr int kLdsSumsMaxK = 64;                           // LDS partial sums up to k = 64
+constexpr int kSortChunk = 1024;
+
+struct KmWork {
+  float* cent;     // [BH, k, 128]
+  float* cc;       // [BH, k]
+  long long* sums; // [BH, k, 128]
+  unsigned* counts;// [BH, k]
+  int32_t* labels; // [BH, N]
+  int32_t* hist;   // [BH, nchunks, k]
+};
+
+// |c|^2 as a fmaf chain in channel order (one lane, reads the centroid from LDS).
+__device__ float centroid_norm(const float* c) {
+  float acc = 0.0f;
+  for (int i = 0; i < kD; ++i) acc = __builtin_fmaf(c[i], c[i], acc);
+  return acc;
+}
+
+__global__ void __launch_bounds__(kD) kmeans_init(const uint16_t* __restrict__ V, int N, int k,
+                                                  KmWork w) {
+  const int c = blockIdx.x, bh = blockIdx.y, i = threadIdx.x;
+  __shared__ float row[kD];
+  const long long src = ((long long)c * N) / k;
+  const float v = bf16_bits_to_f32(V[((long long)bh * N + src) * kD + i]);
+  row[i] = v;
+  const long long ci = ((long long)bh * k + c) * kD + i;
+  w.cent[ci] = v;
+  w.sums[ci] = 0;
+  __syncthreads();
+  if (i == 0) {
+    w.cc[(long long)bh * k + c] = centroid_norm(row);
+    w.counts[(long long)bh * k + c] = 0u;
+  }
+}
+
+template <bool kLdsSums>
+__global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* __restrict__ V, int N,
+                                                                 int k, KmWork w) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int kpad = (k + 3) & ~3;
+  float* centG = reinterpret_cast<float*>(smem);                         // [kpad/4][128][4]
+  float* ccs = centG + kD * kpad;                                         // [kpad]
+  unsigned* cnt = reinterpret_cast<unsigned*>(ccs + kpad);                // [kpad]
+  unsigned long long* psum = reinterpret_cast<unsigned long long*>(cnt + kpad);  // [k][128]
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const float* cent = w.cent + (long long)bh * k * kD;
+  // group-of-four layout: centG[c/4][i][c%4] = centroid c, channel i
+  for (int idx = tid; idx < kpad * kD; idx += kAssignThreads) {
+    const int c = idx / kD, i = idx % kD;
+    centG[((c >> 2) * kD + i) * 4 + (c & 3)] = c < k ? cent[idx] : 0.0f;
+  }
+  for (int c = tid; c < kpad; c += kAssignThreads) {
+    ccs[c] = c < k ? w.cc[(long long)bh * k + c] : __builtin_inff();   // padding never wins
+    cnt[c] = 0u;
+  }
+  if (kLdsSums)
+    for (int idx = tid; idx < k * kD; idx += kAssignThreads) psum[idx] = 0ull;
+  __syncthreads();
+
+  const long long base = (long long)blockIdx.x * kTokPerWG;
+#pragma unroll 1
+  for (int s = 0; s < kTokPerThread; ++s) {
+    const long long j = base + tid + (long long)s * kAssignThreads;
+    if (j >= N) break;
+    const uint16_t* vp = V + ((long long)bh * N + j) * kD;
+    float x[kD];
+#pragma unroll
+    for (int q = 0; q < kD / 8; ++q) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(vp + q * 8);
+      const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[q * 8 + 2 * e] = __uint_as_float(wds[e] << 16);
+        x[q * 8 + 2 * e + 1] = __uint_as_float(wds[e] & 0xFFFF0000u);
+      }
+    }
+    int best = 0;
+    float best_s = __builtin_inff();
+#pragma unroll 1
+    for (int cg = 0; cg < kpad; cg += 4) {
+      const float* grp = centG + cg * kD;
+      float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kD; ++i) {   // fixed order: channel 0..127
+        const float4 c4 = *reinterpret_cast<const float4*>(grp + i * 4);
+        d0 = __builtin_fmaf(x[i], c4.x, d0);
+        d1 = __builtin_fmaf(x[i], c4.y, d1);
+        d2 = __builtin_fmaf(x[i], c4.z, d2);
+        d3 = __builtin_fmaf(x[i], c4.w, d3);
+      }
+      const float sc0 = __builtin_fmaf(-2.0f, d0, ccs[cg + 0]);
+      const float sc1 = __builtin_fmaf(-2.0f, d1, ccs[cg + 1]);
+      const float sc2 = __builtin_fmaf(-2.0f, d2, ccs[cg + 2]);
+      const float sc3 = __builtin_fmaf(-2.0f, d3, ccs[cg + 3]);
+      // strict comparisons in index order: the lowest index wins ties
+      if (sc0 < best_s) { best_s = sc0; best = cg + 0; }
+      if (sc1 < best_s) { best_s = sc1; best = cg + 1; }
+      if (sc2 < best_s) { best_s = sc2; best = cg + 2; }
+      if (sc3 < best_s) { best_s = sc3; best = cg + 3; }
+    }
+    w.labels[(long long)bh * N + j] = best;
+    atomicAdd(&cnt[best], 1u);
+    // fixed-point sums of the token into its cluster (order-free integer adds)
+#pragma unroll
+    for (int i = 0; i < kD; ++i) {
+      const long long qv = (long long)__builtin_rintf(x[i] * 16777216.0f);
+      if (kLdsSums) {
+        atomicAdd(&psum[best * kD + i], (unsigned long long)qv);
+      } else {
+        atomicAdd(reinterpret_cast<unsigned long long*>(w.sums) + ((long long)bh * k + best) * kD + i,
+                  (unsigned long long)qv);
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < k; c += kAssignThreads)
+    if (cnt[c]) atomicAdd(&w.counts[(long long)bh * k + c], cnt[c]);
+  if (kLdsSums) {
+    unsigned long long* gs = reinterpret_cast<unsigned long long*>(w.sums) + (long long)bh * k * kD;
+    for (int idx = tid; idx < k * kD; idx += kAssignThreads)
+      if (psum[idx]) atomicAdd(&gs[idx], psum[idx]);
+  }
+}
+
+__global__ void __launch_bounds__(kD) kmeans_update(int k, KmWork w) {
+  const int c = blockIdx.x, bh = blockIdx.y, i = threadIdx.x;
+  __shared__ float row[kD];
+  const long long ci = ((long long)bh * k + c) * kD + i;
+  const unsigned n = w.counts[(long long)bh * k + c];
+  float v = w.cent[ci];
+  if (n > 0) {
+    const double s = (double)w.sums[ci];
+    v = (float)((s * 0x1p-24) / (double)n);
+    w.cent[ci] = v;
+  }
+  w.sums[ci] = 0;
+  row[i] = v;
+  __syncthreads();
+  if (i == 0) {
+    w.cc[(long long)bh * k + c] = centroid_norm(row);
+    w.counts[(long long)bh * k + c] = 0u;
+  }
+}
+
+__global__ void __launch_bounds__(256) sort_hist(int N, int k, int nchunks, KmWork w) {
+  extern __shared__ unsigned hs[];
+  const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  for (int c = tid; c < k; c += 256) hs[c] = 0u;
+  __syncthreads();
+  const long long base = (long long)chunk * kSortChunk;
+  for (int s = 0; s < kSortChunk / 256; ++s) {
+    const long long j = base + tid + s * 256;
+    if (j < N) atomicAdd(&hs[w.labels[(long long)bh * N + j]], 1u);
+  }
+  __syncthreads();
+  for (int c = tid; c < k; c += 256) w.hist[((long long)bh * nchunks + chunk) * k + c] = (int32_t)hs[c];
+}
+
+// Turns the per-chunk histograms into the first output slot of every (chunk, label).
+__global__ void __launch_bounds__(256) sort_scan(int k, int nchunks, KmWork w) {
+  __shared__ int tot[256];
+  const int bh = blockIdx.x, c = threadIdx.x;
+  int32_t* hist = w.hist + (long long)bh * nchunks * k;
+  int t = 0;
+  if (c < k)
+    for (int ch = 0; ch < nchunks; ++ch) t += hist[(long long)ch * k + c];
+  tot[c] = c < k ? t : 0;
+  __syncthreads();
+  if (c == 0) {
+    int run = 0;
+    for (int q = 0; q < k; ++q) {
+      const int n = tot[q];
+      tot[q] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  if (c < k) {
+    int run = tot[c];
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int n = hist[(long long)ch * k + c];
+      hist[(long long)ch * k + c] = run;
+      run += n;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) sort_scatter(int N, int k, int nchunks, KmWork w,
+                                                    int32_t* __restrict__ perm) {
+  __shared__ int lab[kSortChunk];
+  const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const long long base = (long long)chunk * kSortChunk;
+  const int len = (int)min((long long)kSortChunk, (long long)N - base);
+  for (int q = tid; q < kSortChunk; q += 256) lab[q] = q < len ? w.labels[(long long)bh * N + base + q] : -1;
+  __syncthreads();
+  int mine[kSortChunk / 256], rank[kSortChunk / 256];
+#pragma unroll
+  for (int s = 0; s < kSortChunk / 256; ++s) {
+    mine[s] = lab[tid + s * 256];
+    rank[s] = 0;
+  }
+  // rank = number of earlier tokens of the chunk with the same label (stable order)
+  for (int q = 0; q < len; ++q) {
+    const int lq = lab[q];
+#pragma unroll
+    for (int s = 0; s < kSortChunk / 256; ++s) rank[s] += (lq == mine[s] && q < tid + s * 256) ? 1 : 0;
+  }
+  const int32_t* off = w.hist + ((long long)bh * nchunks + chunk) * k;
+#pragma unroll
+  for (int s = 0; s < kSortChunk / 256; ++s) {
+    const int j = tid + s * 256;
+    if (j < len) perm[(long long)bh * N + off[mine[s]] + rank[s]] = (int32_t)(base + j);
+  }
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct KmLayout {
+  size_t cent, cc, sums, counts, labels, hist, total;
+};
+
+static KmLayout km_layout(long long BH, long long N, int k) {
+  KmLayout L;
+  const long long nchunks = (N + kSortChunk - 1) / kSortChunk;
+  size_t o = 0;
+  L.cent = o;   o += align256(sizeof(float) * BH * k * kD);
+  L.cc = o;     o += align256(sizeof(float) * BH * k);
+  L.sums = o;   o += align256(sizeof(long long) * BH * k * kD);
+  L.counts = o; o += align256(sizeof(unsigned) * BH * k);
+  L.labels = o; o += align256(sizeof(int32_t) * BH * N);
+  L.hist = o;   o += align256(sizeof(int32_t) * BH * nchunks * k);
+  L.total = o;
+  return L;
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" size_t vc_vsmooth_group_workspace(int B, int H, int N, int d, int k) {
+  if (B < 1 || H < 1 || N < 1 || d != kD || k < 1 || k > 256) return 0;
+  return km_layout((long long)B * H, N, k).total;
+}
+
+extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int iters,
+                                int32_t* perm, int32_t* labels, float* centroids, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (d != kD) return VC_ERR_UNSUPPORTED;
+  if (!V || !perm || B < 1 || H < 1 || N < 1 || k < 1 || k > 256 || iters < 1) return VC_ERR_INVALID_ARG;
+  if ((long long)B * H > 65535) return VC_ERR_INVALID_ARG;
+  const long long BH = (long long)B * H;
+  const KmLayout L = km_layout(BH, N, k);
+  if (!workspace || workspace_bytes < L.total) return VC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  KmWork w;
+  w.cent = centroids ? centroids : reinterpret_cast<float*>(ws + L.cent);
+  w.cc = reinterpret_cast<float*>(ws + L.cc);
+  w.sums = reinterpret_cast<long long*>(ws + L.sums);
+  w.counts = reinterpret_cast<unsigned*>(ws + L.counts);
+  w.labels = labels ? labels : reinterpret_cast<int32_t*>(ws + L.labels);
+  w.hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int nchunks = (N + kSortChunk - 1) / kSortChunk;
+  const int kpad = (k + 3) & ~3;
+  const bool lds_sums = k <= kLdsSumsMaxK;
+  const size_t lds = sizeof(float) * (size_t)(kD * kpad + kpad) + sizeof(unsigned) * (size_t)kpad +
+                     (lds_sums ? sizeof(unsigned long long) * (size_t)k * kD : 0);
+  const dim3 gA((N + kTokPerWG - 1) / kTokPerWG, (unsigned)BH);
+
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kmeans_assign<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kmeans_assign<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kmeans_init, dim3(k, (unsigned)BH), dim3(kD), 0, st, V, N, k, w);
+  for (int it = 0; it < iters; ++it) {
+    if (lds_sums)
+      hipLaunchKernelGGL(kmeans_assign<true>, gA, dim3(kAssignThreads), lds, st, V, N, k, w);
+    else
+      hipLaunchKernelGGL(kmeans_assign<false>, gA, dim3(kAssignThreads), lds, st, V, N, k, w);
+    hipLaunchKernelGGL(kmeans_update, dim3(k, (unsigned)BH), dim3(kD), 0, st, k, w);
+  }
+  hipLaunchKernelGGL(sort_hist, dim3(nchunks, (unsigned)BH), dim3(256), sizeof(unsigned) * k, st, N, k,
+                     nchunks, w);
+  hipLaunchKernelGGL(sort_scan, dim3((unsigned)BH), dim3(256), 0, st, k, nchunks, w);
+  hipLaunchKernelGGL(sort_scatter, dim3(nchunks, (unsigned)BH), dim3(256), 0, st, N, k, nchunks, w, perm);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return vc_set_hip_error((int)e);
+  return VC_OK;
+}

@@ -1,0 +1,188 @@
+/*
+ * vc.h -- C ABI of the VC-Attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The method (four web pages about "VC-Attention: Value Smoothing and Softmax
+ * Casting for Low-bit Attention"):
+ *   V-Smooth  -- per batch and head, cluster the Value tokens with k-means,
+ *                reorder Key and Value jointly by cluster label, subtract each
+ *                128-token block's mean from Value, quantise only the residual,
+ *                and add the means back from the online-softmax row sums as one
+ *                outer product per block (paper digest, V-Smooth paragraph;
+ *                news article, section "V-Smooth", items Group/Demean/Restore).
+ *   ExpCast-FP8 -- write each E4M3 probability byte straight from the
+ *                log-domain score with one fused multiply-add, round to nearest
+ *                even, clip to the normal range, beta = -0.35 (paper digest,
+ *                ExpCast-FP8 paragraph; news article, section "ExpCast-FP8").
+ * The pages publish no API; these calls follow their statement of the problem.
+ *
+ * Conventions for every call
+ *   - Every pointer argument is DEVICE memory owned by the caller, except where
+ *     a comment says otherwise.  Arrays are dense and row-major unless a layout
+ *     is spelled out.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on
+ *     it asynchronously; no call allocates, frees or synchronises.
+ *   - Errors in the arguments are reported synchronously as a negative
+ *     vc_status and nothing is enqueued.  A failed kernel launch returns
+ *     VC_ERR_HIP (vc_last_hip_error() gives the HIP code).  Faults during a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Shapes: B batches, H heads, N tokens per (batch, head), d = 128 channels.
+ *     nb = ceil(N / 128) blocks; Np = 128 * nb padded rows.  Rows >= N of every
+ *     code array are written as zero bytes.
+ *   - Preconditions not checked: inputs are finite and |V| < 2^14.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Calls may run concurrently on different streams when their output and
+ *     workspace buffers do not overlap.  The library keeps no global state.
+ */
+#ifndef VC_ATTN_VC_H
+#define VC_ATTN_VC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vc_status {
+  VC_OK = 0,
+  VC_ERR_INVALID_ARG = -1, /* null required pointer, N < 1, B/H < 1, k out of [1,256], iters < 1 */
+  VC_ERR_UNSUPPORTED = -2, /* d != 128, unknown p_mode / v_format, or a mode pairing not built */
+  VC_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than the *_workspace() size */
+  VC_ERR_HIP = -4          /* a HIP launch failed; see vc_last_hip_error() */
+};
+
+/* How the P tile (softmax numerator) is produced inside the attention kernel. */
+enum vc_p_mode {
+  VC_P_EXPCAST = 0,      /* ExpCast-FP8: code = RNE(fmaf(S, 8*kap, 55.65 - 8*mx)), codes < 8 -> 0 */
+  VC_P_FP32EXP_E4M3 = 1, /* conventional: p = exp2(S*kap - mx) in fp32, then E4M3 (RNE) */
+  VC_P_FP32_BF16 = 2     /* fp32 softmax, P rounded to bf16 (the 4-bit path; no ExpCast there) */
+};
+
+/* Format of the V residual codes. */
+enum vc_v_format {
+  VC_V_E4M3 = 0,  /* per-(b,h,channel) scaled E4M3 (8-bit path) */
+  VC_V_NVFP4 = 1  /* E2M1 values, E4M3 scale per 16 tokens, fp32 scale per (b,h) (4-bit path) */
+};
+
+/* ------------------------------------------------------------------------
+ * V-Smooth grouping: k-means over Value tokens per (batch, head), then a stable
+ * sort by cluster label (paper digest, V-Smooth paragraph: "each batch and head
+ * runs online k-means on Value tokens and reorders Key and Value by label";
+ * news article, "V-Smooth", item Group).
+ *
+ * Arithmetic (fixed so that the result is reproducible bit for bit):
+ *   init     centroid c = V[floor(c*N/k)] (as fp32)
+ *   assign   dot = fmaf chain over channels 0..127 from 0, cc = same for c.c,
+ *            score = fmaf(-2, dot, cc), label = argmin, lowest c on ties
+ *   update   int64 sums of llrint(v*2^24) per (cluster, channel), counts;
+ *            centroid = (float)((double)sum * 2^-24 / (double)count);
+ *            an empty cluster keeps its centroid
+ *   iters    (assign, update) repeated `iters` times; labels from the last assign
+ *   sort     stable counting sort: clusters ascending, tokens of a cluster in
+ *            original order
+ *
+ * V          bf16 [B,H,N,128]
+ * perm       out int32 [B,H,N]: perm[b,h,j'] = source token of permuted slot j'
+ * labels     out int32 [B,H,N] cluster label of each ORIGINAL token (nullable)
+ * centroids  out fp32 [B,H,k,128] after the last update (nullable)
+ * workspace  device scratch of at least vc_vsmooth_group_workspace() bytes
+ * ------------------------------------------------------------------------ */
+size_t vc_vsmooth_group_workspace(int B, int H, int N, int d, int k);
+int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int iters,
+                     int32_t* perm, int32_t* labels, float* centroids,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused gather + block mean + quantisation (paper digest, V-Smooth and
+ * preprocessing paragraphs: 128-row blocks subtract their mean, the residual
+ * is quantised -- per-channel E4M3 on the 8-bit path, NVFP4 on the 4-bit path --
+ * the mean is a 16-bit vector; mean, gather and quantisation are fused and no
+ * high-precision intermediate goes back to memory).
+ *
+ * Arithmetic:
+ *   K, V are gathered by perm; blocks are 128 permuted rows (last may be partial).
+ *   mean_t   = bf16_RNE( fp32 sum over ascending rows / n_t )
+ *   R        = fp32(v) - fp32(mean_t)
+ *   E4M3 V   amax_c over all N rows of |R|; sv_c = amax_c/448 (0 if amax_c = 0);
+ *            code = E4M3_RNE_SAT( R * (448/amax_c) )
+ *   NVFP4 V  St = amax_all/2688 per (b,h); per channel and 16 consecutive
+ *            permuted rows (inside a block): sg = E4M3( g_amax / (6*St) ),
+ *            nibble = E2M1_RNE_SAT( R / (dec(sg)*St) )
+ *   K, Q     one scale per 128-row block: s = amax/448, code = E4M3(x*(448/amax));
+ *            K blocks are in permuted order, Q blocks in original order.
+ *
+ * Q          bf16 [B,H,N,128] or NULL (then q_codes/q_scales are not written)
+ * K, V       bf16 [B,H,N,128];  perm int32 [B,H,N] from vc_vsmooth_group
+ * q_codes    out u8 [B,H,Np,128] (original order);  q_scales out fp32 [B,H,nb]
+ * k_codes    out u8 [B,H,Np,128] (permuted order);  k_scales out fp32 [B,H,nb]
+ * v_codes    out, E4M3: u8 [B,H,nb,128(channel),128(row in block)] -- each
+ *            block is stored transposed: the code of permuted row 128*t+u,
+ *            channel c sits at byte ((bh*nb + t)*128 + c)*128 + u.
+ *            NVFP4: u8 [B,H,nb,128(channel),64]: byte ((bh*nb+t)*128+c)*64 + u/2
+ *            holds rows u (low nibble, u even) and u+1 (high nibble).
+ * v_scales   out, E4M3: fp32 [B,H,128] (sv); NVFP4: fp32 [B,H] (St)
+ * v_group_scales  out, NVFP4 only: u8 [B,H,Np/16,128] E4M3 scale codes; NULL for E4M3
+ * v_means    out bf16 [B,H,nb,128]
+ * ------------------------------------------------------------------------ */
+size_t vc_preprocess_workspace(int B, int H, int N, int d, int v_format);
+int vc_preprocess_quant(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                        int B, int H, int N, int d, int v_format,
+                        uint8_t* q_codes, float* q_scales, uint8_t* k_codes, float* k_scales,
+                        uint8_t* v_codes, float* v_scales, uint8_t* v_group_scales,
+                        uint16_t* v_means, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Non-causal low-bit flash attention with block-mean restore (paper digest,
+ * V-Smooth paragraph: "the block mean is added back with one outer product of
+ * the row sums online softmax already accumulates, no second pass over V";
+ * ExpCast-FP8 paragraph for VC_P_EXPCAST).
+ *
+ * For every query row i (original order) and KV block t (permuted order,
+ * ascending -- P codes depend on the running max):
+ *   S     = sum_c dec(q_ic) dec(k_jc)           (FP8 MFMA, fp32 accumulate)
+ *   kap   = fp32(fp32(sq_i * sk_t) * c0),  c0 = fp32(softmax_scale * log2 e)
+ *   mx'   = max(mx, fp32(max_j S * kap))
+ *   P     = ExpCast / exp2 codes of S (see vc_p_mode); keys >= N contribute 0
+ *   l     = 2^(mx-mx') l + sum_j dec(P)
+ *   U     = 2^(mx-mx') U + sum_j dec(P) dec(v_j) + (sum_j dec(P)) mean_t
+ *   O     = U / l  (per-channel V scales applied)
+ * Supported pairings: (EXPCAST | FP32EXP_E4M3) with VC_V_E4M3, FP32_BF16 with
+ * VC_V_NVFP4.  Inputs are the outputs of vc_preprocess_quant (same layouts).
+ * out        fp32 [B,H,N,128], original query order
+ * ------------------------------------------------------------------------ */
+int vc_attn_fp8_fwd(const uint8_t* q_codes, const float* q_scales,
+                    const uint8_t* k_codes, const float* k_scales,
+                    const uint8_t* v_codes, const float* v_scales, const uint8_t* v_group_scales,
+                    const uint16_t* v_means, int B, int H, int N, int d, float softmax_scale,
+                    int p_mode, int v_format, float* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Comparator: standard non-causal flash attention in bf16 (the pages quote all
+ * speed-ups against BF16 FlashAttention-4; this is the in-repo stand-in).
+ * bf16 MFMA for Q.K^T and P.V, online softmax with fp32 exp2, P rounded to bf16.
+ * Q, K, V    bf16 [B,H,N,128];  out fp32 [B,H,N,128]
+ * ------------------------------------------------------------------------ */
+int vc_attn_bf16_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int H, int N,
+                     int d, float softmax_scale, float* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Test hook: vc_attn_fp8_fwd that also records, for every query row and every
+ * padded key slot, the fp32 score S and the P byte the kernel fed to the P.V
+ * product (E4M3 modes only).  s_dump fp32 [B,H,N,Np], p_dump u8 [B,H,N,Np],
+ * key index in permuted order; masked slots get S = 0, P = 0.  Meant for small N
+ * (the dumps are N*Np per head).
+ * ------------------------------------------------------------------------ */
+int vc_attn_fp8_fwd_dump(const uint8_t* q_codes, const float* q_scales,
+                         const uint8_t* k_codes, const float* k_scales,
+                         const uint8_t* v_codes, const float* v_scales, const uint16_t* v_means,
+                         int B, int H, int N, int d, float softmax_scale, int p_mode,
+                         float* out, float* s_dump, uint8_t* p_dump, void* stream);
+
+const char* vc_status_string(int status);
+int vc_last_hip_error(void);
+const char* vc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VC_ATTN_VC_H */

@@ -1,0 +1,206 @@
+"""GPU parity: every entry point of libvc.so against the CPU oracle, element by
+element, on seeded inputs (tiny configuration, the ExpCast ablation, ragged and
+degenerate shapes, and sampled outputs of the full Wan2.2-shaped run).
+
+Bar: bit-exact for labels, permutations, means, scales and every code byte;
+P bytes bit-exact given the kernel's own scores; fp32 outputs within relative
+L2 1e-3 of the oracle."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+import vc_workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(128.0)
+TOL_OUT = 1e-3
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def vc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_attention_video_vc_amd as vc
+    vc.lib()
+    return vc
+
+
+def _u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _run_all(vc, Q, K, V, k, iters, fmt="e4m3"):
+    dev = torch.device("cuda:0")
+    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
+    perm, labels, cents = vc.vsmooth_group(Vd, k, iters, want_labels=True, want_centroids=True)
+    prep = vc.preprocess_quant(Qd, Kd, Vd, perm, fmt)
+    torch.cuda.synchronize()
+    return Qd, Kd, Vd, perm, labels, cents, prep
+
+
+def _check_group_and_codes(vc, Q, K, V, k, iters, heads=None, fmt="e4m3"):
+    """Runs the GPU grouping + preprocessing and checks the listed heads bit for bit."""
+    Qd, Kd, Vd, perm, labels, cents, prep = _run_all(vc, Q, K, V, k, iters, fmt)
+    B, H, N, _ = Q.shape
+    heads = heads or [(b, h) for b in range(B) for h in range(H)]
+    q16, k16, v16 = _u16(Q), _u16(K), _u16(V)
+    perm_c, lab_c, cent_c = perm.cpu().numpy(), labels.cpu().numpy(), cents.cpu().numpy()
+    vcodes = (vc.unswizzle_v_codes(prep["v_codes"], N) if fmt == "e4m3" else prep["v_codes"]).cpu().numpy()
+    preps = {}
+    for (b, h) in heads:
+        lab, cen, _ = O.kmeans(O.bf16_to_f32(v16[b, h]), k, iters)
+        np.testing.assert_array_equal(lab_c[b, h], lab, err_msg=f"labels b{b} h{h}")
+        np.testing.assert_array_equal(cent_c[b, h], cen, err_msg=f"centroids b{b} h{h}")
+        pm = O.stable_label_sort(lab, k)
+        np.testing.assert_array_equal(perm_c[b, h], pm, err_msg=f"perm b{b} h{h}")
+        pr = O.preprocess_head(q16[b, h], k16[b, h], v16[b, h], pm, fmt)
+        np.testing.assert_array_equal(_u16(prep["v_means"][b, h]), pr["means"], err_msg="means")
+        np.testing.assert_array_equal(prep["k_codes"][b, h].cpu().numpy(), pr["k_codes"], err_msg="k codes")
+        np.testing.assert_array_equal(prep["k_scales"][b, h].cpu().numpy(), pr["k_scales"], err_msg="k scales")
+        np.testing.assert_array_equal(prep["q_codes"][b, h].cpu().numpy(), pr["q_codes"], err_msg="q codes")
+        np.testing.assert_array_equal(prep["q_scales"][b, h].cpu().numpy(), pr["q_scales"], err_msg="q scales")
+        if fmt == "e4m3":
+            np.testing.assert_array_equal(vcodes[b, h], pr["v_codes"], err_msg="v codes")
+            np.testing.assert_array_equal(prep["v_scales"][b, h].cpu().numpy(), pr["v_scales"], err_msg="v scales")
+        else:
+            nib = vcodes[b, h]                                  # [nb, 128, 64] packed along rows
+            lo, hi = nib & 15, nib >> 4
+            rows = np.stack([lo, hi], axis=-1).reshape(nib.shape[0], 128, 128)   # [nb, ch, row]
+            rows = rows.transpose(0, 2, 1).reshape(-1, 128)
+            np.testing.assert_array_equal(rows, pr["v_nibbles"], err_msg="nvfp4 nibbles")
+            np.testing.assert_array_equal(prep["v_group_scales"][b, h].cpu().numpy(), pr["v_group_scales"],
+                                          err_msg="nvfp4 group scales")
+            np.testing.assert_array_equal(prep["v_scales"][b, h].cpu().numpy(), pr["v_scales"][0],
+                                          err_msg="nvfp4 St")
+        preps[(b, h)] = pr
+    return prep, preps, (Qd, Kd, Vd)
+
+
+def _check_attention(vc, prep, preps, p_mode, rows_per_head=None):
+    out = vc.attn_fp8_fwd(prep, SCALE, p_mode).cpu().numpy()
+    errs = []
+    for (b, h), pr in preps.items():
+        N = pr["N"]
+        rows = np.arange(N) if rows_per_head is None else rows_per_head
+        ref = O.vc_attention_head(pr, SCALE, p_mode, rows=rows)
+        e = O.rel_l2(out[b, h][rows], ref)
+        errs.append(e)
+        assert e <= TOL_OUT, f"rel-L2 {e:.2e} vs oracle, b{b} h{h} {p_mode}"
+    return out, max(errs)
+
+
+def test_config0_tiny_8bit_end_to_end(vc):
+    _say("config 0: B1 H2 N1024 k8 T10, E4M3 + ExpCast")
+    c = W.CONFIGS[0]
+    Q, K, V = W.make_inputs(0)
+    prep, preps, _ = _check_group_and_codes(vc, Q, K, V, c["k"], c["iters"])
+    _check_attention(vc, prep, preps, "expcast")
+
+
+def test_config0_p_bytes_given_scores(vc):
+    _say("config 0: dump S and P bytes; replay ExpCast on the kernel's scores")
+    c = W.CONFIGS[0]
+    Q, K, V = W.make_inputs(0)
+    prep, preps, _ = _check_group_and_codes(vc, Q, K, V, c["k"], c["iters"])
+    out, S, P = vc.attn_fp8_fwd_dump(prep, SCALE, "expcast")
+    S, P = S.cpu().numpy(), P.cpu().numpy()
+    for (b, h), pr in preps.items():
+        N = pr["N"]
+        nb = O.n_blocks(N)
+        sq = pr["q_scales"][np.arange(N) // 128]
+        kap = [O.f32(O.f32(sq * pr["k_scales"][t]) * O.score_scale(SCALE)) for t in range(nb)]
+        tiles = [S[b, h][:, t * 128:(t + 1) * 128] for t in range(nb)]
+        replay = O.expcast_given_scores(tiles, kap, N)
+        for t in range(nb):
+            np.testing.assert_array_equal(P[b, h][:, t * 128:(t + 1) * 128], replay[t],
+                                          err_msg=f"P bytes given S, b{b} h{h} tile {t}")
+        # scores themselves against the exact fp64 product rounded once
+        rec = []
+        O.vc_attention_head(pr, SCALE, "expcast", record=rec)
+        S_or = np.concatenate([np.pad(r["S"], ((0, 0), (0, 128 - r["S"].shape[1]))) for r in rec], axis=1)
+        diff = S[b, h] != S_or
+        rel = np.abs(S[b, h] - S_or) / np.maximum(np.abs(S_or), 1e-30)
+        _say(f"  b{b} h{h}: scores differing from RNE(exact) {diff.mean():.4f}, max rel {rel.max():.2e}")
+        assert rel.max() < 1e-5
+
+
+def test_config1_expcast_ablation_both_p_paths(vc):
+    _say("config 1: B1 H8 N8192 k32 T10, conventional and ExpCast P paths")
+    c = W.CONFIGS[1]
+    Q, K, V = W.make_inputs(1)
+    heads = [(0, 0), (0, 5)]
+    prep, preps, _ = _check_group_and_codes(vc, Q, K, V, c["k"], c["iters"], heads=heads)
+    rows = np.concatenate([np.arange(0, 8192, 61), np.arange(8100, 8192)])
+    _check_attention(vc, prep, preps, "fp32exp_e4m3", rows)
+    _check_attention(vc, prep, preps, "expcast", rows)
+
+
+@pytest.mark.parametrize("B,H,N,k,iters", [(1, 3, 1000, 8, 4), (2, 1, 129, 3, 2), (1, 1, 1, 1, 1),
+                                           (1, 2, 127, 5, 3), (1, 1, 300, 256, 2), (1, 1, 700, 100, 3)])
+def test_ragged_and_degenerate_shapes(vc, B, H, N, k, iters):
+    _say(f"ragged: B{B} H{H} N{N} k{k} T{iters}")
+    Q, K, V = W.custom_inputs(B, H, N, seed=N + k, recipe="clustered")
+    prep, preps, _ = _check_group_and_codes(vc, Q, K, V, k, iters)
+    _check_attention(vc, prep, preps, "expcast")
+    _check_attention(vc, prep, preps, "fp32exp_e4m3")
+
+
+def test_constant_value_blocks(vc):
+    _say("degenerate: V constant per 128-row block (zero residual, zero V scales)")
+    N = 384
+    Q, K, _ = W.custom_inputs(1, 1, N, seed=5)
+    rows = torch.randn(3, 128, generator=torch.Generator().manual_seed(1)) * 4
+    V = rows.repeat_interleave(128, dim=0).reshape(1, 1, N, 128).to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    perm = torch.arange(N, dtype=torch.int32, device=dev).reshape(1, 1, N)
+    prep = vc.preprocess_quant(Q.to(dev), K.to(dev), V.to(dev), perm)
+    assert not prep["v_codes"].any() and not prep["v_scales"].any()
+    pr = O.preprocess_head(_u16(Q[0, 0]), _u16(K[0, 0]), _u16(V[0, 0]), np.arange(N, dtype=np.int32))
+    out = vc.attn_fp8_fwd(prep, SCALE, "expcast").cpu().numpy()[0, 0]
+    assert O.rel_l2(out, O.vc_attention_head(pr, SCALE, "expcast")) <= TOL_OUT
+
+
+def test_deterministic_bitwise(vc):
+    _say("determinism: two runs of config 0 compared bit for bit")
+    c = W.CONFIGS[0]
+    Q, K, V = W.make_inputs(0)
+    r1 = _run_all(vc, Q, K, V, c["k"], c["iters"])
+    r2 = _run_all(vc, Q, K, V, c["k"], c["iters"])
+    assert torch.equal(r1[3], r2[3])
+    o1 = vc.attn_fp8_fwd(r1[6], SCALE)
+    o2 = vc.attn_fp8_fwd(r2[6], SCALE)
+    assert torch.equal(o1, o2)
+
+
+def test_bf16_comparator_matches_exact_attention(vc):
+    _say("bf16 comparator: B1 H2 N1000 against exact fp64 attention")
+    Q, K, V = W.custom_inputs(1, 2, 1000, seed=11, recipe="clustered")
+    dev = torch.device("cuda:0")
+    out = vc.attn_bf16_fwd(Q.to(dev), K.to(dev), V.to(dev), SCALE).cpu().numpy()
+    for h in range(2):
+        ex = O.exact_attention(_u16(Q[0, h]), _u16(K[0, h]), _u16(V[0, h]), SCALE)
+        # P is rounded to bf16 (relative error <= 2^-9 per element)
+        assert O.rel_l2(out[0, h], ex) < 4e-3
+
+
+def test_wan22_full_size_sampled(vc):
+    """Full Wan2.2 shape (B1 H40 N75600, k64, T8) in the launch configuration the
+    bench times; the oracle checks two heads' grouping and codes in full and 48
+    sampled query rows of each against its attention output."""
+    _say("config 2/3: B1 H40 N75600 k64 T8 full size, sampled oracle heads 0 and 39")
+    c = W.CONFIGS[2]
+    Q, K, V = W.make_inputs(2)
+    heads = [(0, 0), (0, 39)]
+    prep, preps, _ = _check_group_and_codes(vc, Q, K, V, c["k"], c["iters"], heads=heads)
+    rows = np.concatenate([np.arange(0, 75600, 1601), np.arange(75590, 75600)])
+    _check_attention(vc, prep, preps, "expcast", rows)
