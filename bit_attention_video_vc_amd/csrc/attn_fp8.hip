@@ -23,9 +23,13 @@
 //    swizzle that keeps the 128-bit operand reads free of bank conflicts.
 //  * the row sum of the decoded P bytes comes from one extra MFMA against an
 //    all-ones operand (exact: every E4M3 value is a multiple of 2^-9), and the
-//    block mean is restored as U += rowsum (x) mean_t / sv with fp32 FMAs.
+//    block mean is restored as U += rowsum (x) mean_t / sv with a rank-2 fp32
+//    MFMA per two KV blocks, so no VALU instruction touches the accumulators
+//    except the (rare) rescale when a running max moves.
 //  * workgroups are ordered head-major and handed to the 8 XCDs in contiguous
 //    ranges, so the workgroups sharing an XCD's L2 stream the same K/V blocks.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace vc {
@@ -44,11 +48,15 @@ struct AttnArgs {
   float c0;
 };
 
+__device__ __forceinline__ v16f mfma_f32x2(float a, float b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 template <int kPMode, bool kDump>
-__global__ void __launch_bounds__(kAttnThreads) attn_fp8_e4m3(AttnArgs a) {
+__global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(AttnArgs a) {
   __shared__ __align__(16) uint8_t Ks[2][kTile];
   __shared__ __align__(16) uint8_t Vs[2][kTile];
-  __shared__ __align__(16) float Mu[2][kD];
+  __shared__ __align__(16) float MuT[2][kD];   // mean_t / sv, stored [col][cb]: channel 32*cb + col
   __shared__ float InvSv[kD];
   __shared__ float Sv[kD];
 
@@ -91,18 +99,26 @@ __global__ void __launch_bounds__(kAttnThreads) attn_fp8_e4m3(AttnArgs a) {
   // 8j + i/8 at chunk position i%8, so it fetches the global chunk that the
   // XOR swizzle puts there.
   uint32_t mr = 0;
+  uint32_t dkoff[4], dvoff[4];   // in-tile byte offsets of this lane's 16-byte DMA chunks
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (4 * i + wave) + (lane >> 3), pos = lane & 7;
+    dkoff[i] = (uint32_t)(row * kD + 16 * (pos ^ swz_k(row)));
+    dvoff[i] = (uint32_t)(row * kD + 16 * (pos ^ swz_v(row)));
+  }
   auto load_tile = [&](int t, int buf) {
+    const uint8_t* kt = kbase + (long long)t * kTile;
+    const uint8_t* vt = vbase + (long long)t * kTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * i + wave;
-      const int row = 8 * j + (lane >> 3), pos = lane & 7;
-      dma16(kbase + (long long)t * kTile + row * kD + 16 * (pos ^ swz_k(row)), &Ks[buf][1024 * j]);
-      dma16(vbase + (long long)t * kTile + row * kD + 16 * (pos ^ swz_v(row)), &Vs[buf][1024 * j]);
+      dma16(kt + dkoff[i], &Ks[buf][1024 * j]);
+      dma16(vt + dvoff[i], &Vs[buf][1024 * j]);
     }
     if (tid < kD) mr = mbase[(long long)t * kD + tid];
   };
   auto store_means = [&](int buf) {
-    if (tid < kD) Mu[buf][tid] = bf16_bits_to_f32(mr) * InvSv[tid];
+    if (tid < kD) MuT[buf][(tid & 31) * 4 + (tid >> 5)] = bf16_bits_to_f32(mr) * InvSv[tid];
   };
 
   load_tile(0, 0);
@@ -121,9 +137,37 @@ __global__ void __launch_bounds__(kAttnThreads) attn_fp8_e4m3(AttnArgs a) {
   v8i ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0
+  // mean restore is batched over two KV blocks: lanes of group g hold block
+  // (2m + g)'s row sum (B operand of a rank-2 fp32 MFMA) and its mean/sv values
+  // for their channel in each 32-channel block (A operand).
+  float abat = 0.0f;
+  float mbat[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // LDS operand addresses: the K rows sigma(m, col) of the four 32-key blocks
+  // differ by multiples of 16 rows and the V rows 32*cb + col by multiples of 32,
+  // neither of which changes the swizzle, so four base offsets per operand plus
+  // compile-time offsets cover every read.
+  uint32_t lk[4], lv[4];
+  {
+    const int kr = sigma(0, col), ksw = swz_k(kr), vsw = swz_v(col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 4 * (i >> 1) + 2 * g + (i & 1);    // chunks 2g, 2g+1, 4+2g, 5+2g
+      lk[i] = (uint32_t)(kr * kD + 16 * (c ^ ksw));
+      lv[i] = (uint32_t)(col * kD + 16 * (c ^ vsw));
+    }
+  }
+  auto ld16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
+  auto op8 = [](uint4 lo, uint4 hi) {
+    v8i r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+  };
 
-  for (int t = 0; t < nb; ++t) {
-    const int buf = t & 1;
+  // one KV block; the LDS buffer index is a compile-time constant so every
+  // LDS address is a base register plus an immediate offset
+  auto step = [&](const int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     if (t + 1 < nb) load_tile(t + 1, buf ^ 1);
 
     // ---- S^T = K_t . Q^T : 4 blocks of 32 keys x 32 queries ----
@@ -132,11 +176,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_fp8_e4m3(AttnArgs a) {
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[m][r] = 0.0f;
-      const int row = sigma(m, col);
-      const uint8_t* rb = &Ks[buf][row * kD];
-      const int sw = swz_k(row);
+      const uint8_t* kb = &Ks[buf][kD * (64 * (m >> 1) + 16 * (m & 1))];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) s[m] = mfma32(lds_op(rb, 4 * c2 + 2 * g, sw), qop[c2], s[m]);
+      for (int c2 = 0; c2 < 2; ++c2)
+        s[m] = mfma32(op8(ld16(kb + lk[2 * c2]), ld16(kb + lk[2 * c2 + 1])), qop[c2], s[m]);
     }
     // keys beyond N (last tile only) take no part
     if ((t + 1) * kBlock > N) {
@@ -165,22 +208,23 @@ __global__ void __launch_bounds__(kAttnThreads) attn_fp8_e4m3(AttnArgs a) {
       const float Bc = 55.65f - 8.0f * mx_new;
       // codes never exceed 56 unless rounding of a huge running max pushes the
       // row maximum past 56.5; then clamp (the oracle clamps at 56 as well)
-      const bool clamp = __any(__builtin_fmaf(M, A, Bc) >= 56.5f);
+      if (__builtin_expect(__any(__builtin_fmaf(M, A, Bc) >= 56.5f), 0)) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[m][r] = fminf(s[m][r], (56.0f - Bc) / A);
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           uint32_t w = 0u;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            float cf = __builtin_fmaf(s[m][4 * r4 + b], A, Bc);
-            if (clamp) cf = fminf(cf, 56.0f);
-            w = __builtin_amdgcn_cvt_pk_u8_f32(cf, b, w);   // round to nearest even, clamp [0,255]
-          }
+          for (int b = 0; b < 4; ++b)   // round to nearest even, clamp to [0,255], pack
+            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[m][4 * r4 + b], A, Bc), b, w);
           // flush codes 1..7 (below the E4M3 normal range) to 0, four bytes at a time
           const uint32_t keep = (w + 0x78787878u) & 0x80808080u;
-          w &= (keep >> 1) - (keep >> 7);
-          pk[4 * m + r4] = w;
+          pk[4 * m + r4] = w & (keep - (keep >> 7));
         }
     } else {   // VC_P_FP32EXP_E4M3: conventional exp2 then E4M3 conversion
 #pragma unroll
@@ -217,6 +261,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_fp8_e4m3(AttnArgs a) {
         for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
     }
     l *= alpha;
+    abat *= alpha;
     mx = mx_new;
 
     // ---- O^T += V^T_t . P^T ; row sums from an all-ones operand ----
@@ -230,29 +275,40 @@ __global__ void __launch_bounds__(kAttnThreads) attn_fp8_e4m3(AttnArgs a) {
       for (int i = 0; i < 8; ++i) pop[i] = (int)pk[8 * h + i];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const int ch = 32 * cb + col;
-        o[cb] = mfma32(lds_op(&Vs[buf][ch * kD], 4 * h + 2 * g, swz_v(ch)), pop, o[cb]);
+        const uint8_t* vb = &Vs[buf][kD * 32 * cb];
+        o[cb] = mfma32(op8(ld16(vb + lv[2 * h]), ld16(vb + lv[2 * h + 1])), pop, o[cb]);
       }
       rs = mfma32(ones, pop, rs);
     }
     const float rsum = rs[0];
     l += rsum;
-    // ---- mean restore: U += rowsum (x) mean_t / sv ----
+    // ---- mean restore: U += rowsum (x) mean_t / sv, two blocks per rank-2 MFMA ----
+    {
+      const float4 mu = *reinterpret_cast<const float4*>(&MuT[buf][col * 4]);
+      const bool mine = g == buf;
+      abat = mine ? rsum : abat;
+      mbat[0] = mine ? mu.x : mbat[0];
+      mbat[1] = mine ? mu.y : mbat[1];
+      mbat[2] = mine ? mu.z : mbat[2];
+      mbat[3] = mine ? mu.w : mbat[3];
+      if (buf == 1 || t + 1 == nb) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 mu = *reinterpret_cast<const float4*>(&Mu[buf][32 * cb + 8 * a4 + 4 * g]);
-        o[cb][4 * a4 + 0] = __builtin_fmaf(rsum, mu.x, o[cb][4 * a4 + 0]);
-        o[cb][4 * a4 + 1] = __builtin_fmaf(rsum, mu.y, o[cb][4 * a4 + 1]);
-        o[cb][4 * a4 + 2] = __builtin_fmaf(rsum, mu.z, o[cb][4 * a4 + 2]);
-        o[cb][4 * a4 + 3] = __builtin_fmaf(rsum, mu.w, o[cb][4 * a4 + 3]);
+        for (int cb = 0; cb < 4; ++cb) o[cb] = mfma_f32x2(mbat[cb], abat, o[cb]);
+        abat = 0.0f;
       }
+    }
 
     if (t + 1 < nb) store_means(buf ^ 1);
     wait_dma();
     __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 1 < nb; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < nb) step(t, std::integral_constant<int, 0>{});
 
   // ---- epilogue: O = sv * U / l, original query order ----
   if (qrow < N) {

@@ -404,7 +404,7 @@ def exp2_probs_f32(S: np.ndarray, kap: np.ndarray, mx: np.ndarray) -> np.ndarray
 # ---------------------------------------------------------------------------
 
 def online_attention(Qd, Kd, Vres, means, N, qscale_rows, kscales, c0, p_mode, rows,
-                     record=None):
+                     record=None, scores=None):
     """Blockwise non-causal attention with online softmax and block-mean restore.
 
     For each KV block t in permuted order (the order matters: P codes depend on
@@ -422,7 +422,9 @@ def online_attention(Qd, Kd, Vres, means, N, qscale_rows, kscales, c0, p_mode, r
     sums online softmax already accumulates, with one outer product and no second
     pass over V.  [news] "V-Smooth", item Restore.
     Qd, Kd: decoded codes (float64); Vres: residual in real units (float64 [N, d]);
-    means: float64 [nb, d].  rows: the query rows to compute."""
+    means: float64 [nb, d].  rows: the query rows to compute.
+    scores: optional float32 [N, >= N] scores to use in place of Q.K^T (to replay
+    the method on a device's own scores, key index in permuted order)."""
     nb = n_blocks(N)
     R = len(rows)
     d = Vres.shape[1]
@@ -433,7 +435,7 @@ def online_attention(Qd, Kd, Vres, means, N, qscale_rows, kscales, c0, p_mode, r
     U = np.zeros((R, d))
     for t in range(nb):
         k0, k1 = t * BLOCK, min(N, (t + 1) * BLOCK)
-        S64 = q @ Kd[k0:k1].T
+        S64 = q @ Kd[k0:k1].T if scores is None else f32(scores[rows][:, k0:k1]).astype(np.float64)
         kap = f32(f32(sq * F32(kscales[t])) * F32(c0))
         if p_mode == "exact":          # no rounding anywhere (used to pin the algebra)
             x = S64 * kap.astype(np.float64)[:, None]
@@ -467,9 +469,10 @@ def online_attention(Qd, Kd, Vres, means, N, qscale_rows, kscales, c0, p_mode, r
     return U / l[:, None]
 
 
-def vc_attention_head(prep: dict, softmax_scale: float, p_mode: str, rows=None, record=None):
+def vc_attention_head(prep: dict, softmax_scale: float, p_mode: str, rows=None, record=None, scores=None):
     """VC attention output (float64 [rows, d], original query order) for one
-    (batch, head) from the preprocessed codes of preprocess_head()."""
+    (batch, head) from the preprocessed codes of preprocess_head().  `scores`
+    optionally replaces the exact Q.K^T (see online_attention)."""
     N = prep["N"]
     if rows is None:
         rows = np.arange(N)
@@ -479,7 +482,7 @@ def vc_attention_head(prep: dict, softmax_scale: float, p_mode: str, rows=None, 
     means = bf16_to_f32(prep["means"]).astype(np.float64)
     sq = prep["q_scales"][rows // BLOCK]
     return online_attention(Qd, Kd, prep["v_res"], means, N, sq, prep["k_scales"],
-                            score_scale(softmax_scale), p_mode, rows, record)
+                            score_scale(softmax_scale), p_mode, rows, record, scores)
 
 
 def expcast_given_scores(S_tiles, kap_tiles, N):

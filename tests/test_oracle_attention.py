@@ -114,3 +114,12 @@ def test_nvfp4_path_runs_and_tracks_exact():
     out = O.vc_attention_head(preps[0][0], SCALE, "fp32_bf16")
     ex = O.exact_attention(q[0, 0], k[0, 0], v[0, 0], SCALE)
     assert O.rel_l2(out, ex) < 0.2
+
+
+def test_replay_with_given_scores_equals_computed_scores():
+    q, k, v, perm, preps = _prep_cfg(400, seed=7)
+    pr = preps[0][0]
+    rec = []
+    base = O.vc_attention_head(pr, SCALE, "expcast", record=rec)
+    S = np.concatenate([np.pad(r["S"], ((0, 0), (0, 128 - r["S"].shape[1]))) for r in rec], axis=1)
+    np.testing.assert_array_equal(O.vc_attention_head(pr, SCALE, "expcast", scores=S), base)
