@@ -42,7 +42,9 @@ def lib():
         L.vc_preprocess_workspace.restype = Z
         L.vc_preprocess_quant.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
         L.vc_attn_fp8_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, P]
-        L.vc_attn_bf16_fwd.argtypes = [P, P, P, I, I, I, I, F, P, P]
+        L.vc_attn_bf16_workspace.argtypes = [I, I, I, I]
+        L.vc_attn_bf16_workspace.restype = Z
+        L.vc_attn_bf16_fwd.argtypes = [P, P, P, I, I, I, I, F, P, P, Z, P]
         L.vc_attn_fp8_fwd_dump.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P]
         for f in ("vc_vsmooth_group", "vc_preprocess_quant", "vc_attn_fp8_fwd", "vc_attn_bf16_fwd",
                   "vc_attn_fp8_fwd_dump"):
@@ -174,7 +176,7 @@ def attn_fp8_fwd_dump(prep: dict, softmax_scale: float | None = None, p_mode="ex
     return out, s, p
 
 
-def attn_bf16_fwd(Q, K, V, softmax_scale: float | None = None, out=None):
+def attn_bf16_fwd(Q, K, V, softmax_scale: float | None = None, out=None, workspace=None):
     """bf16 flash-attention comparator; returns fp32 [B,H,N,128]."""
     dev = _dev(_bits(Q))
     _dev(_bits(K))
@@ -184,8 +186,12 @@ def attn_bf16_fwd(Q, K, V, softmax_scale: float | None = None, out=None):
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
-    _check(lib().vc_attn_bf16_fwd(_ptr(Q), _ptr(K), _ptr(V), B, H, N, d, float(softmax_scale), _ptr(out),
-                                  _stream(dev)), "vc_attn_bf16_fwd")
+    L = lib()
+    ws_bytes = L.vc_attn_bf16_workspace(B, H, N, d)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(L.vc_attn_bf16_fwd(_ptr(Q), _ptr(K), _ptr(V), B, H, N, d, float(softmax_scale), _ptr(out),
+                              _ptr(workspace), ws_bytes, _stream(dev)), "vc_attn_bf16_fwd")
     return out
 
 

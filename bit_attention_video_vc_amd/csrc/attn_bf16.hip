@@ -5,31 +5,34 @@
 // Faster Generation"; paper digest, results table).  This kernel is the in-repo
 // stand-in on MI355X: bf16 V_MFMA_F32_32X32X16_BF16 for Q.K^T and P.V, online
 // softmax with fp32 exp2, P rounded to bf16 (round to nearest even), row sums
-// of the rounded P.
+// accumulated in fp32.
 //
-// Same lane organisation as the FP8 kernel: S^T = K.Q^T so that each lane holds
-// one query's scores and the bf16 P values are already in the B-operand layout
-// of O^T = V^T.P^T.  V is transposed into LDS while it is staged.
+// Same organisation as the FP8 kernel: S^T = K.Q^T so each lane holds one
+// query's scores and the bf16 P values are already in the B-operand layout of
+// O^T = V^T.P^T.  A first kernel writes V transposed per 128-key block into the
+// caller's workspace (one HBM pass); the attention kernel then streams K and V^T
+// tiles global -> LDS directly, double buffered, 8 wavefronts (256 queries) per
+// workgroup so that two wavefronts share each SIMD.
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace vc {
 
-constexpr int kB16Threads = 256;
-constexpr int kRowB = kD * 2;   // bytes per bf16 row (256)
-
-typedef short v4s __attribute__((ext_vector_type(4)));
+constexpr int kB16Threads = 512;
+constexpr int kRowB = kD * 2;            // bytes per bf16 row (256)
+constexpr int kTileB = kBlock * kRowB;   // bytes per bf16 tile (32 KiB)
 
 struct B16Args {
-  const uint16_t* q; const uint16_t* k; const uint16_t* v;
+  const uint16_t* q; const uint16_t* k; const uint16_t* vt;
   float* out;
-  int N, nb, BH;
+  int N, nb, nqb, BH;
   float c0;
 };
 
 __device__ __forceinline__ int swz_kb(int row) {
   return (row & 3) | (((row >> 2) & 1) << 2) | (((row >> 5) & 1) << 3);
 }
-__device__ __forceinline__ int swz_vb(int row) { return row & 15; }
 
 __device__ __forceinline__ v16f mfma_bf16(const v8bf& a, const v8bf& b, const v16f& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -41,19 +44,43 @@ __device__ __forceinline__ v8bf as_bf(uint4 u) {
   return r;
 }
 
-__global__ void __launch_bounds__(kB16Threads) attn_bf16_kernel(B16Args a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* Kt = smem;                     // [2][128 keys][256 B]
-  uint8_t* Vt = smem + 2 * kBlock * kRowB; // [2][128 ch][256 B] (transposed)
+// V [BH][N][128] -> V^T per block: vt[BH][nb][128 ch][128 keys], zero past N.
+__global__ void __launch_bounds__(256) transpose_v_bf16(const uint16_t* __restrict__ V, int N, int nb,
+                                                        uint16_t* __restrict__ vt) {
+  __shared__ __align__(16) uint16_t tile[kBlock * (kD + 8)];   // padded rows
+  const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int n = min(kBlock, N - t * kBlock);
+  for (int q = tid; q < kBlock * 16; q += 256) {
+    const int r = q >> 4, c = q & 15;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < n) v = *reinterpret_cast<const uint4*>(V + ((long long)bh * N + t * kBlock + r) * kD + 8 * c);
+    *reinterpret_cast<uint4*>(&tile[r * (kD + 8) + 8 * c]) = v;
+  }
+  __syncthreads();
+  uint16_t* dst = vt + ((long long)bh * nb + t) * kBlock * kD;
+  for (int q = tid; q < kD * 16; q += 256) {
+    const int ch = q & (kD - 1), kc = q >> 7;   // channel, chunk of 8 keys
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[(8 * kc + 2 * e) * (kD + 8) + ch] |
+             ((uint32_t)tile[(8 * kc + 2 * e + 1) * (kD + 8) + ch] << 16);
+    *reinterpret_cast<uint4*>(dst + ch * kBlock + 8 * kc) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
 
-  const int nqb = a.nb;
-  const int item = xcd_item(blockIdx.x, nqb * a.BH);
-  const int bh = item / nqb, qb = item % nqb;
+__global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* Kt = smem;                 // [2][128 keys][256 B], swizzled chunks
+  uint8_t* Vt = smem + 2 * kTileB;    // [2][128 ch][256 B], swizzled chunks
+
+  const int item = xcd_item(blockIdx.x, a.nqb * a.BH);
+  const int bh = item / a.nqb, qb = item % a.nqb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, col = lane & 31;
   const int N = a.N, nb = a.nb;
 
-  const int qrow = qb * kBlock + wave * 32 + col;
+  const int qrow = qb * 256 + wave * 32 + col;
   v8bf qop[8];
   {
     const uint16_t* qp = a.q + ((long long)bh * N + min(qrow, N - 1)) * kD;
@@ -65,51 +92,46 @@ __global__ void __launch_bounds__(kB16Threads) attn_bf16_kernel(B16Args a) {
     }
   }
   const uint16_t* kbase = a.k + (long long)bh * N * kD;
-  const uint16_t* vbase = a.v + (long long)bh * N * kD;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vt + (long long)bh * nb * kBlock * kD);
 
-  // K tile: global -> LDS directly (instruction j of 32 fills LDS bytes
-  // [1024j, 1024j+1024): lane i writes row 4j + i/16 at chunk position i%16).
-  // V tile: staged through registers and written transposed.
-  auto load_k = [&](int t, int buf) {
-    uint8_t* K = Kt + buf * kBlock * kRowB;
+  // DMA: instruction j (32 per operand per tile, 4 per wave) fills LDS bytes
+  // [1024j, 1024j+1024) = rows 4j..4j+3; lane i writes row 4j + i/16 at chunk
+  // position i%16.
+  uint32_t dk_row[4], dk_pos[4], dvoff[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = 4 * i + wave;
-      const int row = 4 * j + (lane >> 4), pos = lane & 15;
-      const int key = min(t * kBlock + row, N - 1);   // rows past N are masked later
-      dma16(kbase + (long long)key * kD + 8 * (pos ^ swz_kb(row)), K + 1024 * j);
+  for (int i = 0; i < 4; ++i) {
+    const int j = 8 * i + wave;
+    const int row = 4 * j + (lane >> 4), pos = lane & 15;
+    dk_row[i] = (uint32_t)row;
+    dk_pos[i] = (uint32_t)(8 * (pos ^ swz_kb(row)));            // element offset in the K row
+    dvoff[i] = (uint32_t)(row * kRowB + 16 * (pos ^ (row & 15)));
+  }
+  auto load_tile = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 8 * i + wave;
+      const int key = min(t * kBlock + (int)dk_row[i], N - 1);   // rows past N are masked later
+      dma16(kbase + (long long)key * kD + dk_pos[i], Kt + buf * kTileB + 1024 * j);
+      dma16(vbase + (long long)t * kTileB + dvoff[i], Vt + buf * kTileB + 1024 * j);
     }
   };
-  uint4 vr[8];
-  auto load_v = [&](int t) {
+  // LDS operand addresses (rows sigma(m, col) share the K swizzle, channels
+  // 32*cb + col share the V^T swizzle)
+  uint32_t lk[8], lv[8];
+  {
+    const int kr = sigma(0, col), ksw = swz_kb(kr), vsw = col & 15;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int qd = tid + kB16Threads * i;
-      const int vkey_local = qd & 127, vch = qd >> 7;          // consecutive keys per wave
-      const int vkey = t * kBlock + vkey_local;
-      vr[i] = vkey < N ? *reinterpret_cast<const uint4*>(vbase + (long long)vkey * kD + 8 * vch)
-                       : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_v = [&](int buf) {
-    uint8_t* V = Vt + buf * kBlock * kRowB;
+    for (int j = 0; j < 8; ++j) lk[j] = (uint32_t)(kr * kRowB + 16 * ((2 * j + g) ^ ksw));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int qd = tid + kB16Threads * i;
-      const int key = qd & 127, c0 = 8 * (qd >> 7);
-      const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = c0 + e;
-        const uint16_t val = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-        *reinterpret_cast<uint16_t*>(V + c * kRowB + 16 * ((key >> 3) ^ swz_vb(c)) + 2 * (key & 7)) = val;
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int chunk = 8 * (m >> 1) + 4 * g + 2 * (m & 1) + s2;
+        lv[2 * m + s2] = (uint32_t)(col * kRowB + 16 * (chunk ^ vsw));
       }
-    }
-  };
+  }
 
-  load_k(0, 0);
-  load_v(0);
-  store_v(0);
+  load_tile(0, 0);
   wait_dma();
   __syncthreads();
 
@@ -120,23 +142,20 @@ __global__ void __launch_bounds__(kB16Threads) attn_bf16_kernel(B16Args a) {
     for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
   float mx = -__builtin_inff(), l = 0.0f;
 
-  for (int t = 0; t < nb; ++t) {
-    const int buf = t & 1;
-    const uint8_t* K = Kt + buf * kBlock * kRowB;
-    const uint8_t* V = Vt + buf * kBlock * kRowB;
-    if (t + 1 < nb) load_k(t + 1, buf ^ 1);
+  auto step = [&](const int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const uint8_t* K = Kt + buf * kTileB;
+    const uint8_t* V = Vt + buf * kTileB;
+    if (t + 1 < nb) load_tile(t + 1, buf ^ 1);
 
     v16f s[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[m][r] = 0.0f;
-      const int row = sigma(m, col);
-      const uint8_t* rb = K + row * kRowB;
-      const int sw = swz_kb(row);
+      const uint8_t* kb = K + kRowB * (64 * (m >> 1) + 16 * (m & 1));
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        s[m] = mfma_bf16(as_bf(*reinterpret_cast<const uint4*>(rb + 16 * ((2 * j + g) ^ sw))), qop[j], s[m]);
+      for (int j = 0; j < 8; ++j) s[m] = mfma_bf16(as_bf(*reinterpret_cast<const uint4*>(kb + lk[j])), qop[j], s[m]);
     }
     if ((t + 1) * kBlock > N) {
 #pragma unroll
@@ -163,39 +182,45 @@ __global__ void __launch_bounds__(kB16Threads) attn_bf16_kernel(B16Args a) {
     }
     l *= alpha;
     mx = mx_new;
+    const float nmx = -mx_new;
 
-    if (t + 1 < nb) load_v(t + 1);
     float rsum = 0.0f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
+        typedef float v2f __attribute__((ext_vector_type(2)));
+        typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
         uint32_t pw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(s[m][8 * s2 + 2 * e] * a.c0 - mx_new);
-          const float p1 = __builtin_amdgcn_exp2f(s[m][8 * s2 + 2 * e + 1] * a.c0 - mx_new);
-          const uint32_t b0 = f32_to_bf16_rne(p0), b1 = f32_to_bf16_rne(p1);
-          rsum += __uint_as_float(b0 << 16) + __uint_as_float(b1 << 16);
-          pw[e] = b0 | (b1 << 16);
+          v2f p;
+          p.x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][8 * s2 + 2 * e], a.c0, nmx));
+          p.y = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][8 * s2 + 2 * e + 1], a.c0, nmx));
+          rsum += p.x + p.y;
+          const v2bf pb = __builtin_convertvector(p, v2bf);   // round to nearest even
+          pw[e] = __builtin_bit_cast(uint32_t, pb);
         }
         const v8bf pop = as_bf(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-        const int keyoff = 64 * (m >> 1) + 32 * g + 16 * (m & 1) + 8 * s2;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          const int ch = 32 * cb + col;
-          const uint4 vv = *reinterpret_cast<const uint4*>(V + ch * kRowB + 16 * ((keyoff >> 3) ^ swz_vb(ch)));
+          const uint4 vv = *reinterpret_cast<const uint4*>(V + kRowB * 32 * cb + lv[2 * m + s2]);
           o[cb] = mfma_bf16(as_bf(vv), pop, o[cb]);
         }
       }
     }
     rsum += __shfl_xor(rsum, 32);
     l += rsum;
-
-    if (t + 1 < nb) store_v(buf ^ 1);
     wait_dma();
     __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 1 < nb; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < nb) step(t, std::integral_constant<int, 0>{});
 
   if (qrow < N) {
     const float invl = 1.0f / l;
@@ -219,22 +244,35 @@ __global__ void __launch_bounds__(kB16Threads) attn_bf16_kernel(B16Args a) {
 
 using namespace vc;
 
+extern "C" size_t vc_attn_bf16_workspace(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d != kD) return 0;
+  const long long nb = (N + kBlock - 1) / kBlock;
+  return (size_t)B * H * nb * kTileB;
+}
+
 extern "C" int vc_attn_bf16_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int H, int N,
-                                int d, float softmax_scale, float* out, void* stream) {
+                                int d, float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   if (d != kD) return VC_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !out || B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
+  if ((long long)B * H > 65535) return VC_ERR_INVALID_ARG;
   const int nb = (N + kBlock - 1) / kBlock;
-  if ((long long)nb * B * H > 0x7FFFFFFFLL) return VC_ERR_INVALID_ARG;
-  B16Args a{Q, K, V, out, N, nb, B * H, score_scale_c0(softmax_scale)};
-  const size_t lds = 4u * kBlock * kRowB;   // 128 KiB: double-buffered K and V^T
+  const int nqb = (N + 255) / 256;
+  if ((long long)nqb * B * H > 0x7FFFFFFFLL) return VC_ERR_INVALID_ARG;
+  const size_t need = vc_attn_bf16_workspace(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return VC_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* vt = static_cast<uint16_t*>(workspace);
+  hipLaunchKernelGGL(transpose_v_bf16, dim3(nb, B * H), dim3(256), 0, st, V, N, nb, vt);
+  B16Args a{Q, K, vt, out, N, nb, nqb, B * H, score_scale_c0(softmax_scale)};
+  const size_t lds = 4u * kTileB;   // 128 KiB: double-buffered K and V^T
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bf16_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)(nb * B * H)), dim3(kB16Threads), lds,
-                     static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)(nqb * B * H)), dim3(kB16Threads), lds, st, a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VC_OK : vc_set_hip_error((int)e);
 }

@@ -14,8 +14,8 @@
 //
 // Kernels (all on the caller's stream, launched T times for assign/update):
 //   kmeans_init     centroid c <- V[floor(c*N/k)], zero the accumulators, |c|^2
-//   kmeans_assign   one token per lane, centroids in LDS in groups of four (one
-//                   128-bit LDS read feeds four independent FMA chains); labels;
+//   kmeans_assign   one token per lane, four independent FMA chains (centroids
+//                   read through the scalar cache: uniform addresses); labels;
 //                   fixed-point sums into LDS (k <= 64) then one global atomic
 //                   per non-zero partial
 //   kmeans_update   new centroids, zero the accumulators, |c|^2
@@ -24,9 +24,9 @@
 
 namespace vc {
 
-constexpr int kAssignThreads = 512;
+constexpr int kAssignThreads = 256;
 constexpr int kTokPerThread = 2;
-constexpr int kTokPerWG = kAssignThreads * kTokPerThread;  // 1024 tokens
+constexpr int kTokPerWG = kAssignThreads * kTokPerThread;  // 512 tokens
 constexpr int kLdsSumsMaxK = 64;                           // LDS partial sums up to k = 64
 constexpr int kSortChunk = 1024;
 
@@ -67,22 +67,15 @@ template <bool kLdsSums>
 __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* __restrict__ V, int N,
                                                                  int k, KmWork w) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int kpad = (k + 3) & ~3;
-  float* centG = reinterpret_cast<float*>(smem);                         // [kpad/4][128][4]
-  float* ccs = centG + kD * kpad;                                         // [kpad]
-  unsigned* cnt = reinterpret_cast<unsigned*>(ccs + kpad);                // [kpad]
-  unsigned long long* psum = reinterpret_cast<unsigned long long*>(cnt + kpad);  // [k][128]
+  unsigned* cnt = reinterpret_cast<unsigned*>(smem);                                   // [k]
+  unsigned long long* psum = reinterpret_cast<unsigned long long*>(smem + 8 * ((k + 1) / 2));  // [k][128]
   const int bh = blockIdx.y, tid = threadIdx.x;
-  const float* cent = w.cent + (long long)bh * k * kD;
-  // group-of-four layout: centG[c/4][i][c%4] = centroid c, channel i
-  for (int idx = tid; idx < kpad * kD; idx += kAssignThreads) {
-    const int c = idx / kD, i = idx % kD;
-    centG[((c >> 2) * kD + i) * 4 + (c & 3)] = c < k ? cent[idx] : 0.0f;
-  }
-  for (int c = tid; c < kpad; c += kAssignThreads) {
-    ccs[c] = c < k ? w.cc[(long long)bh * k + c] : __builtin_inff();   // padding never wins
-    cnt[c] = 0u;
-  }
+  // Centroids and |c|^2 are read with wave-uniform addresses: the compiler turns
+  // them into scalar loads, so every FMA takes its centroid value from an SGPR
+  // and the centroids cost no LDS bandwidth.
+  const float* __restrict__ C = w.cent + (long long)bh * k * kD;
+  const float* __restrict__ ccg = w.cc + (long long)bh * k;
+  for (int c = tid; c < k; c += kAssignThreads) cnt[c] = 0u;
   if (kLdsSums)
     for (int idx = tid; idx < k * kD; idx += kAssignThreads) psum[idx] = 0ull;
   __syncthreads();
@@ -91,8 +84,8 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* 
 #pragma unroll 1
   for (int s = 0; s < kTokPerThread; ++s) {
     const long long j = base + tid + (long long)s * kAssignThreads;
-    if (j >= N) break;
-    const uint16_t* vp = V + ((long long)bh * N + j) * kD;
+    const bool live = j < N;
+    const uint16_t* vp = V + ((long long)bh * N + (live ? j : 0)) * kD;
     float x[kD];
 #pragma unroll
     for (int q = 0; q < kD / 8; ++q) {
@@ -106,39 +99,48 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* 
     }
     int best = 0;
     float best_s = __builtin_inff();
+    const int k4 = k & ~3;
 #pragma unroll 1
-    for (int cg = 0; cg < kpad; cg += 4) {
-      const float* grp = centG + cg * kD;
+    for (int c = 0; c < k4; c += 4) {
       float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
 #pragma unroll
       for (int i = 0; i < kD; ++i) {   // fixed order: channel 0..127
-        const float4 c4 = *reinterpret_cast<const float4*>(grp + i * 4);
-        d0 = __builtin_fmaf(x[i], c4.x, d0);
-        d1 = __builtin_fmaf(x[i], c4.y, d1);
-        d2 = __builtin_fmaf(x[i], c4.z, d2);
-        d3 = __builtin_fmaf(x[i], c4.w, d3);
+        d0 = __builtin_fmaf(x[i], C[(c + 0) * kD + i], d0);
+        d1 = __builtin_fmaf(x[i], C[(c + 1) * kD + i], d1);
+        d2 = __builtin_fmaf(x[i], C[(c + 2) * kD + i], d2);
+        d3 = __builtin_fmaf(x[i], C[(c + 3) * kD + i], d3);
       }
-      const float sc0 = __builtin_fmaf(-2.0f, d0, ccs[cg + 0]);
-      const float sc1 = __builtin_fmaf(-2.0f, d1, ccs[cg + 1]);
-      const float sc2 = __builtin_fmaf(-2.0f, d2, ccs[cg + 2]);
-      const float sc3 = __builtin_fmaf(-2.0f, d3, ccs[cg + 3]);
+      const float sc0 = __builtin_fmaf(-2.0f, d0, ccg[c + 0]);
+      const float sc1 = __builtin_fmaf(-2.0f, d1, ccg[c + 1]);
+      const float sc2 = __builtin_fmaf(-2.0f, d2, ccg[c + 2]);
+      const float sc3 = __builtin_fmaf(-2.0f, d3, ccg[c + 3]);
       // strict comparisons in index order: the lowest index wins ties
-      if (sc0 < best_s) { best_s = sc0; best = cg + 0; }
-      if (sc1 < best_s) { best_s = sc1; best = cg + 1; }
-      if (sc2 < best_s) { best_s = sc2; best = cg + 2; }
-      if (sc3 < best_s) { best_s = sc3; best = cg + 3; }
+      if (sc0 < best_s) { best_s = sc0; best = c + 0; }
+      if (sc1 < best_s) { best_s = sc1; best = c + 1; }
+      if (sc2 < best_s) { best_s = sc2; best = c + 2; }
+      if (sc3 < best_s) { best_s = sc3; best = c + 3; }
     }
-    w.labels[(long long)bh * N + j] = best;
-    atomicAdd(&cnt[best], 1u);
-    // fixed-point sums of the token into its cluster (order-free integer adds)
+#pragma unroll 1
+    for (int c = k4; c < k; ++c) {
+      float d0 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kD; ++i) {
-      const long long qv = (long long)__builtin_rintf(x[i] * 16777216.0f);
-      if (kLdsSums) {
-        atomicAdd(&psum[best * kD + i], (unsigned long long)qv);
-      } else {
-        atomicAdd(reinterpret_cast<unsigned long long*>(w.sums) + ((long long)bh * k + best) * kD + i,
-                  (unsigned long long)qv);
+      for (int i = 0; i < kD; ++i) d0 = __builtin_fmaf(x[i], C[c * kD + i], d0);
+      const float sc0 = __builtin_fmaf(-2.0f, d0, ccg[c]);
+      if (sc0 < best_s) { best_s = sc0; best = c; }
+    }
+    if (live) {
+      w.labels[(long long)bh * N + j] = best;
+      atomicAdd(&cnt[best], 1u);
+      // fixed-point sums of the token into its cluster (order-free integer adds)
+#pragma unroll
+      for (int i = 0; i < kD; ++i) {
+        const long long qv = (long long)__builtin_rintf(x[i] * 16777216.0f);
+        if (kLdsSums) {
+          atomicAdd(&psum[best * kD + i], (unsigned long long)qv);
+        } else {
+          atomicAdd(reinterpret_cast<unsigned long long*>(w.sums) + ((long long)bh * k + best) * kD + i,
+                    (unsigned long long)qv);
+        }
       }
     }
   }
@@ -291,10 +293,8 @@ extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, i
   w.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int nchunks = (N + kSortChunk - 1) / kSortChunk;
-  const int kpad = (k + 3) & ~3;
   const bool lds_sums = k <= kLdsSumsMaxK;
-  const size_t lds = sizeof(float) * (size_t)(kD * kpad + kpad) + sizeof(unsigned) * (size_t)kpad +
-                     (lds_sums ? sizeof(unsigned long long) * (size_t)k * kD : 0);
+  const size_t lds = 8 * (size_t)((k + 1) / 2) + (lds_sums ? sizeof(unsigned long long) * (size_t)k * kD : 0);
   const dim3 gA((N + kTokPerWG - 1) / kTokPerWG, (unsigned)BH);
 
   static bool attr_set = false;

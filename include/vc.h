@@ -158,12 +158,18 @@ int vc_attn_fp8_fwd(const uint8_t* q_codes, const float* q_scales,
 
 /* ------------------------------------------------------------------------
  * Comparator: standard non-causal flash attention in bf16 (the pages quote all
- * speed-ups against BF16 FlashAttention-4; this is the in-repo stand-in).
- * bf16 MFMA for Q.K^T and P.V, online softmax with fp32 exp2, P rounded to bf16.
+ * speed-ups against BF16 FlashAttention-4: insight article, section "A Faster
+ * Kernel Does Not Automatically Mean Faster Generation"; this is the in-repo
+ * stand-in).  bf16 MFMA for Q.K^T and P.V, online softmax with fp32 exp2, P
+ * rounded to bf16.  The call first writes V transposed per 128-key block into
+ * the workspace (one HBM pass), then runs the attention kernel.
  * Q, K, V    bf16 [B,H,N,128];  out fp32 [B,H,N,128]
+ * workspace  device scratch of at least vc_attn_bf16_workspace() bytes
  * ------------------------------------------------------------------------ */
+size_t vc_attn_bf16_workspace(int B, int H, int N, int d);
 int vc_attn_bf16_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int H, int N,
-                     int d, float softmax_scale, float* out, void* stream);
+                     int d, float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* ------------------------------------------------------------------------
  * Test hook: vc_attn_fp8_fwd that also records, for every query row and every
