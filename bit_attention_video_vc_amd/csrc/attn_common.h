@@ -44,6 +44,19 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* lds_wave_base) 
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
+// Buffer-resource form of the same copy: the tile base stays in scalar
+// registers (descriptor + soffset) and each lane adds a 32-bit offset, so no
+// per-lane 64-bit address is kept live across a loop.  The descriptor's record
+// count bounds every access: offsets at or past `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base, uint32_t voff,
+                                          uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           (int)voff, (int)soff, 0, 0);
+}
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 float score_scale_c0(float softmax_scale);

@@ -52,10 +52,32 @@ __device__ __forceinline__ v16f mfma_f32x2(float a, float b, const v16f& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// MFMA bursts run at raised wave priority: the SIMD's other wavefront is then
+// usually in its VALU phase, and the arbiter interleaves the two.
+__device__ __forceinline__ void mfma_phase_begin() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void mfma_phase_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int kPMode, bool kDump>
 __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(AttnArgs a) {
-  __shared__ __align__(16) uint8_t Ks[2][kTile];
-  __shared__ __align__(16) uint8_t Vs[2][kTile];
+  // The two buffers of each operand are separate LDS objects so that reads of
+  // one are not ordered behind the asynchronous copies into the other (the
+  // copies are tracked by the vector memory counter).
+  __shared__ __align__(16) uint8_t Ks0[kTile];
+  __shared__ __align__(16) uint8_t Ks1[kTile];
+  __shared__ __align__(16) uint8_t Vs0[kTile];
+  __shared__ __align__(16) uint8_t Vs1[kTile];
   __shared__ __align__(16) float MuT[2][kD];   // mean_t / sv, stored [col][cb]: channel 32*cb + col
   __shared__ float InvSv[kD];
   __shared__ float Sv[kD];
@@ -63,7 +85,8 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
   const int nqb = a.nb;
   const int item = xcd_item(blockIdx.x, nqb * a.BH);
   const int bh = item / nqb, qb = item % nqb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
   const int g = lane >> 5, col = lane & 31;
   const int N = a.N, nb = a.nb;
   const long long Np = (long long)nb * kBlock;
@@ -88,7 +111,9 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
       qop[c2][4] = hi.x; qop[c2][5] = hi.y; qop[c2][6] = hi.z; qop[c2][7] = hi.w;
     }
   }
-  const float sq = a.qs[(long long)bh * nb + qb];
+  // uniform: held in a scalar register, so no wait on it inside the tile loop
+  const float sq = __builtin_bit_cast(
+      float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.qs[(long long)bh * nb + qb])));
 
   const uint8_t* kbase = a.k + (long long)bh * Np * kD;
   const uint8_t* vbase = a.v + (long long)bh * nb * kTile;
@@ -98,30 +123,43 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
   // 4 per wave) fills LDS bytes [1024j, 1024j+1024): lane i writes row
   // 8j + i/8 at chunk position i%8, so it fetches the global chunk that the
   // XOR swizzle puts there.
+  // The copies go through buffer resources (one head's nb tiles each), so the
+  // tile offset is a scalar and a lane keeps only 32-bit in-tile offsets.
+  // Rows of instructions i and i+2 differ by 64, which leaves swz_k unchanged,
+  // and rows of any two differ by a multiple of 32, which leaves swz_v
+  // unchanged: three lane offsets plus scalar offsets cover all eight copies.
   uint32_t mr = 0;
-  uint32_t dkoff[4], dvoff[4];   // in-tile byte offsets of this lane's 16-byte DMA chunks
+  float ksn = 0.0f;   // K scale of the block in flight; becomes the next block's
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)nb * kTile);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)nb * kTile);
+  uint32_t dkoff[2], dvoff;
+  {
+    const int pos = lane & 7;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * (4 * i + wave) + (lane >> 3), pos = lane & 7;
-    dkoff[i] = (uint32_t)(row * kD + 16 * (pos ^ swz_k(row)));
-    dvoff[i] = (uint32_t)(row * kD + 16 * (pos ^ swz_v(row)));
+    for (int i = 0; i < 2; ++i) {
+      const int row = 8 * (4 * i + wave) + (lane >> 3);
+      dkoff[i] = (uint32_t)(row * kD + 16 * (pos ^ swz_k(row)));
+    }
+    const int row = 8 * wave + (lane >> 3);
+    dvoff = (uint32_t)(row * kD + 16 * (pos ^ swz_v(row)));
   }
   auto load_tile = [&](int t, int buf) {
-    const uint8_t* kt = kbase + (long long)t * kTile;
-    const uint8_t* vt = vbase + (long long)t * kTile;
+    const uint32_t toff = (uint32_t)t * kTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * i + wave;
-      dma16(kt + dkoff[i], &Ks[buf][1024 * j]);
-      dma16(vt + dvoff[i], &Vs[buf][1024 * j]);
+      dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * j, dkoff[i & 1], toff + 8192u * (i >> 1));
+      dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * j, dvoff, toff + 4096u * i);
     }
     if (tid < kD) mr = mbase[(long long)t * kD + tid];
+    ksn = a.ks[(long long)bh * nb + t];   // K scale of the block being copied
   };
   auto store_means = [&](int buf) {
     if (tid < kD) MuT[buf][(tid & 31) * 4 + (tid >> 5)] = bf16_bits_to_f32(mr) * InvSv[tid];
   };
 
   load_tile(0, 0);
+  float ksc = ksn;
   __syncthreads();          // InvSv ready
   store_means(0);
   wait_dma();
@@ -134,9 +172,19 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
     for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
   float mx = -__builtin_inff();
   float l = 0.0f;
+  // Row sums come from V_MFMA_F32_16X16X128_F8F6F4 with a P half (64 keys) as
+  // the B operand: B lane l is column l%16 of k-group l/16, which holds query
+  // l%32 over 32 of the half's keys.  A lane l (row l%16, k-group l/16) is E4M3
+  // 1.0 when bit 2 of the row equals the parity of the k-group and 0 otherwise,
+  // so output row r sums the two k-groups of query (r%8 < 4 ? col : col + 16).
+  // Output lane l holds rows 4(l/16)..4(l/16)+3 of column l%16, which is the
+  // row sum of query l%32: the lane's own query.
   v8i ones;
+  {
+    const int on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0
+    for (int i = 0; i < 8; ++i) ones[i] = on ? 0x38383838 : 0;
+  }
   // mean restore is batched over two KV blocks: lanes of group g hold block
   // (2m + g)'s row sum (B operand of a rank-2 fp32 MFMA) and its mean/sv values
   // for their channel in each 32-channel block (A operand).
@@ -171,16 +219,18 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
     if (t + 1 < nb) load_tile(t + 1, buf ^ 1);
 
     // ---- S^T = K_t . Q^T : 4 blocks of 32 keys x 32 queries ----
+    mfma_phase_begin();
     v16f s[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[m][r] = 0.0f;
-      const uint8_t* kb = &Ks[buf][kD * (64 * (m >> 1) + 16 * (m & 1))];
+      const uint8_t* kb = (buf ? Ks1 : Ks0) + kD * (64 * (m >> 1) + 16 * (m & 1));
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
         s[m] = mfma32(op8(ld16(kb + lk[2 * c2]), ld16(kb + lk[2 * c2 + 1])), qop[c2], s[m]);
     }
+    mfma_phase_end();
     // keys beyond N (last tile only) take no part
     if ((t + 1) * kBlock > N) {
 #pragma unroll
@@ -198,7 +248,7 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
 #pragma unroll
       for (int r = 0; r < 16; ++r) M = fmaxf(M, s[m][r]);
     M = fmaxf(M, __shfl_xor(M, 32));
-    const float kap = (sq * a.ks[(long long)bh * nb + t]) * a.c0;
+    const float kap = (sq * ksc) * a.c0;
     const float mx_new = fmaxf(mx, M * kap);
 
     // ---- P bytes, laid out as the B operand of the P.V MFMA ----
@@ -265,9 +315,8 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
     mx = mx_new;
 
     // ---- O^T += V^T_t . P^T ; row sums from an all-ones operand ----
-    v16f rs;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rs[r] = 0.0f;
+    mfma_phase_begin();
+    v4f rs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       v8i pop;
@@ -275,10 +324,10 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
       for (int i = 0; i < 8; ++i) pop[i] = (int)pk[8 * h + i];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const uint8_t* vb = &Vs[buf][kD * 32 * cb];
+        const uint8_t* vb = (buf ? Vs1 : Vs0) + kD * 32 * cb;
         o[cb] = mfma32(op8(ld16(vb + lv[2 * h]), ld16(vb + lv[2 * h + 1])), pop, o[cb]);
       }
-      rs = mfma32(ones, pop, rs);
+      rs = mfma16(ones, pop, rs);
     }
     const float rsum = rs[0];
     l += rsum;
@@ -297,10 +346,12 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
         abat = 0.0f;
       }
     }
+    mfma_phase_end();
 
     if (t + 1 < nb) store_means(buf ^ 1);
     wait_dma();
     __syncthreads();
+    ksc = ksn;
   };
 
   int t = 0;
