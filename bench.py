@@ -14,11 +14,20 @@ on the stream it runs on, against MI355X's dense FP8 MFMA peak.
 cpu_baseline: the CPU oracle on one head (grouping, preprocessing and a sample of
 query rows), extrapolated to the whole job.
 
+fidelity: rel-L2 of the attention output against exact fp32 attention (fp32
+matmuls and softmax on the GPU) over sampled query rows of every head.
+roofline.traffic: HBM bytes per attention launch from the committed rocprofv3
+counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's
+reading for a plain 1 GiB copy); null when the kernel sources differ from the
+ones the counters were taken on.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --profile {attn,group,copy}   (short runs for rocprofv3)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -30,6 +39,8 @@ sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 CFG = 2
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fp8_e4m3_wan22_traffic.md")
+ATTN_SOURCES = ("attn_fp8.hip", "attn_common.h", "vc_common.h")
 
 
 def parse():
@@ -39,7 +50,54 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--profile", choices=("attn", "group", "copy"), default=None,
+                    help="short run for a profiler: attention kernel only, grouping + preprocessing "
+                         "(Q skipped), or a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
+
+
+def attn_source_sha256():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "bit_attention_video_vc_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None
+    if it is missing or was taken on other kernel sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_SUMMARY) as fh:
+            for line in fh:
+                if line.startswith("- ") and ":" in line:
+                    k, v = line[2:].split(":", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("kernel_sources_sha256") != attn_source_sha256():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def fidelity(Qd, Kd, Vd, out, scale, rows_per_head=64):
+    """rel-L2 of out against exact fp32 attention on sampled query rows."""
+    import torch
+    B, H, N, d = Qd.shape
+    rows = torch.linspace(0, N - 1, rows_per_head, device=Qd.device).round().long()
+    num = den = 0.0
+    for b in range(B):
+        for h in range(H):
+            q = Qd[b, h].index_select(0, rows).float()
+            k = Kd[b, h].float()
+            v = Vd[b, h].float()
+            p = torch.softmax((q @ k.t().contiguous()) * scale, dim=-1)
+            ref = p @ v
+            got = out[b, h].index_select(0, rows)
+            num += float(((got - ref) ** 2).sum())
+            den += float((ref ** 2).sum())
+    return math.sqrt(num / den), f"{rows_per_head} evenly spaced query rows of each of {B * H} heads"
 
 
 def timed(fn, reps, stream):
@@ -103,6 +161,15 @@ def main():
     import bit_attention_video_vc_amd as vc
     import vc_workloads as W
 
+    if args.profile == "copy":
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print("[bench] copied 1 GiB device to device", file=sys.stderr, flush=True)
+        return
+
     c = W.CONFIGS[CFG]
     B, H, N = c["B"], c["H"], c["N"]
     scale = 1.0 / math.sqrt(128.0)
@@ -113,6 +180,20 @@ def main():
     Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
     out = torch.empty(B, H, N, 128, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.profile == "group":
+        for _ in range(2):
+            perm, _, _ = vc.vsmooth_group(Vd, c["k"], c["iters"])
+            vc.preprocess_quant(None, Kd, Vd, perm)
+        torch.cuda.synchronize()
+        print("[bench] grouping + preprocessing (Q skipped) x2 done", file=sys.stderr, flush=True)
+        return
+    if args.profile == "attn":
+        perm, _, _ = vc.vsmooth_group(Vd, c["k"], c["iters"])
+        prep = vc.preprocess_quant(Qd, Kd, Vd, perm)
+        ms_attn = timed(lambda: vc.attn_fp8_fwd(prep, scale, "expcast", out=out), args.kernel_reps, stream)
+        print(f"[bench] attention x{args.kernel_reps}: {ms_attn:.3f} ms per call", file=sys.stderr, flush=True)
+        return
 
     state = {}
 
@@ -142,6 +223,13 @@ def main():
     print(f"[bench] group {ms_group:.2f} ms, preprocess {ms_prep:.2f} ms, attention {ms_attn:.2f} ms, "
           f"bf16 comparator {ms_bf16:.2f} ms", file=sys.stderr, flush=True)
 
+    # fidelity against exact fp32 attention on sampled rows (fp8 path, then bf16 comparator)
+    vc.attn_fp8_fwd(prep, scale, "expcast", out=out)
+    fid_fp8, fid_rows = fidelity(Qd, Kd, Vd, out, scale)
+    vc.attn_bf16_fwd(Qd, Kd, Vd, scale, out=out)
+    fid_bf16, _ = fidelity(Qd, Kd, Vd, out, scale)
+    print(f"[bench] rel-L2 vs exact fp32: fp8 {fid_fp8:.3e}, bf16 {fid_bf16:.3e}", file=sys.stderr, flush=True)
+
     flops = 4.0 * N * N * 128 * H * B
     value = flops / (ms * 1e-3) / 1e12
     achieved = flops / (ms_attn * 1e-3) / 1e12
@@ -159,20 +247,23 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic (seeded Wan2.2-shaped stand-in for model activations)",
         "config": {
-            "workload": "wan2.2-14b self-attention, B=1 H=40 N=75600 d=128; V-Smooth k=64 T=8, "
+            "workload": "wan2.2-14b-shaped self-attention, B=1 H=40 N=75600 d=128; V-Smooth k=64 T=8, "
                         "E4M3 residual, ExpCast P; step = grouping + preprocess + attention",
-            "global_batch": B,
-            "seq_len": N,
+            "batch": B,
             "heads": H,
-            "parallelism": "none (1 GPU)",
+            "seq_len": N,
+            "head_dim": 128,
         },
         "stages_ms": {"vsmooth_group": round(ms_group, 3), "preprocess_quant": round(ms_prep, 3),
                       "attn_fp8_expcast": round(ms_attn, 3)},
         "attn_kernel_tflops": round(achieved, 1),
         "bf16_comparator": {"ms": round(ms_bf16, 3), "tflops": round(flops / (ms_bf16 * 1e-3) / 1e12, 1),
                             "speedup_of_fp8_kernel": round(ms_bf16 / ms_attn, 3)},
+        "fidelity_rel_l2_vs_exact_fp32": {"attn_fp8_expcast": float(f"{fid_fp8:.4e}"),
+                                          "attn_bf16": float(f"{fid_bf16:.4e}"), "rows": fid_rows},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": committed_traffic()},
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
