@@ -31,7 +31,9 @@
  *   - Preconditions not checked: inputs are finite and |V| < 2^14.
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Calls may run concurrently on different streams when their output and
- *     workspace buffers do not overlap.  The library keeps no global state.
+ *     workspace buffers do not overlap.  The only state the library keeps is the
+ *     HIP error code of the calling thread's last failed launch
+ *     (vc_last_hip_error), held per thread.
  */
 #ifndef VC_ATTN_VC_H
 #define VC_ATTN_VC_H
