@@ -56,6 +56,13 @@ __device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, const v4f& c) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// max of a lane's value and that of lane l ^ 32, without LDS (V_PERMLANE32_SWAP)
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
 // MFMA bursts run at raised wave priority: the SIMD's other wavefront is then
 // usually in its VALU phase, and the arbiter interleaves the two.
 __device__ __forceinline__ void mfma_phase_begin() {
@@ -247,7 +254,7 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) M = fmaxf(M, s[m][r]);
-    M = fmaxf(M, __shfl_xor(M, 32));
+    M = max_across_halves(M);
     const float kap = (sq * ksc) * a.c0;
     const float mx_new = fmaxf(mx, M * kap);
 
