@@ -14,10 +14,12 @@
 //
 // Kernels (all on the caller's stream, launched T times for assign/update):
 //   kmeans_init     centroid c <- V[floor(c*N/k)], zero the accumulators, |c|^2
-//   kmeans_assign   one token per lane, four independent FMA chains (centroids
-//                   read through the scalar cache: uniform addresses); labels;
-//                   fixed-point sums into LDS (k <= 64) then one global atomic
-//                   per non-zero partial
+//   kmeans_assign   labels and counts: one token per lane, four independent FMA
+//                   chains (centroids read through the scalar cache: uniform
+//                   addresses)
+//   kmeans_accum    fixed-point sums: tokens one at a time, lanes over channels,
+//                   into LDS (k <= 64; conflict-free), then one global atomic
+//                   per non-zero partial of the 2048-token block
 //   kmeans_update   new centroids, zero the accumulators, |c|^2
 //   sort_hist / sort_scan / sort_scatter   stable counting sort by label
 #include "vc_common.h"
@@ -27,6 +29,8 @@ namespace vc {
 constexpr int kAssignThreads = 256;
 constexpr int kTokPerThread = 2;
 constexpr int kTokPerWG = kAssignThreads * kTokPerThread;  // 512 tokens
+constexpr int kAccThreads = 256;
+constexpr int kAccTok = 2048;                              // tokens per accumulation workgroup
 constexpr int kLdsSumsMaxK = 64;                           // LDS partial sums up to k = 64
 constexpr int kSortChunk = 1024;
 
@@ -63,12 +67,9 @@ __global__ void __launch_bounds__(kD) kmeans_init(const uint16_t* __restrict__ V
   }
 }
 
-template <bool kLdsSums>
-__global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* __restrict__ V, int N,
-                                                                 int k, KmWork w) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  unsigned* cnt = reinterpret_cast<unsigned*>(smem);                                   // [k]
-  unsigned long long* psum = reinterpret_cast<unsigned long long*>(smem + 8 * ((k + 1) / 2));  // [k][128]
+__global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* __restrict__ V, int N, int k,
+                                                                 KmWork w) {
+  __shared__ unsigned cnt[256];
   const int bh = blockIdx.y, tid = threadIdx.x;
   // Centroids and |c|^2 are read with wave-uniform addresses: the compiler turns
   // them into scalar loads, so every FMA takes its centroid value from an SGPR
@@ -76,16 +77,14 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* 
   const float* __restrict__ C = w.cent + (long long)bh * k * kD;
   const float* __restrict__ ccg = w.cc + (long long)bh * k;
   for (int c = tid; c < k; c += kAssignThreads) cnt[c] = 0u;
-  if (kLdsSums)
-    for (int idx = tid; idx < k * kD; idx += kAssignThreads) psum[idx] = 0ull;
   __syncthreads();
 
   const long long base = (long long)blockIdx.x * kTokPerWG;
 #pragma unroll 1
   for (int s = 0; s < kTokPerThread; ++s) {
     const long long j = base + tid + (long long)s * kAssignThreads;
-    const bool live = j < N;
-    const uint16_t* vp = V + ((long long)bh * N + (live ? j : 0)) * kD;
+    if (j >= N) break;
+    const uint16_t* vp = V + ((long long)bh * N + j) * kD;
     float x[kD];
 #pragma unroll
     for (int q = 0; q < kD / 8; ++q) {
@@ -128,29 +127,65 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* 
       const float sc0 = __builtin_fmaf(-2.0f, d0, ccg[c]);
       if (sc0 < best_s) { best_s = sc0; best = c; }
     }
-    if (live) {
-      w.labels[(long long)bh * N + j] = best;
-      atomicAdd(&cnt[best], 1u);
-      // fixed-point sums of the token into its cluster (order-free integer adds)
-#pragma unroll
-      for (int i = 0; i < kD; ++i) {
-        const long long qv = (long long)__builtin_rintf(x[i] * 16777216.0f);
-        if (kLdsSums) {
-          atomicAdd(&psum[best * kD + i], (unsigned long long)qv);
-        } else {
-          atomicAdd(reinterpret_cast<unsigned long long*>(w.sums) + ((long long)bh * k + best) * kD + i,
-                    (unsigned long long)qv);
-        }
-      }
-    }
+    w.labels[(long long)bh * N + j] = best;
+    atomicAdd(&cnt[best], 1u);
   }
   __syncthreads();
   for (int c = tid; c < k; c += kAssignThreads)
     if (cnt[c]) atomicAdd(&w.counts[(long long)bh * k + c], cnt[c]);
+}
+
+// Fixed-point sums of every cluster: int64 sum of rint(v * 2^24) per (cluster,
+// channel).  Tokens go one at a time with lanes over channels: lane l takes
+// channels 2l and 2l+1 (one 32-bit load), and the LDS partials are laid out so
+// that both adds of a token hit 64 consecutive 8-byte slots of the token's
+// cluster row (slot h*64 + l holds channel 2l + h); they never collide.  The
+// integer adds are order-free, so any split of the tokens gives the same sums.
+template <bool kLdsSums>
+__global__ void __launch_bounds__(kAccThreads) kmeans_accum(const uint16_t* __restrict__ V, int N, int k,
+                                                              KmWork w) {
+  extern __shared__ __align__(16) unsigned long long psum[];   // [k][128] when kLdsSums
+  const int bh = blockIdx.y, tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  if (kLdsSums)
+    for (int idx = tid; idx < k * kD; idx += kAccThreads) psum[idx] = 0ull;
+  __syncthreads();
+  unsigned long long* gs = reinterpret_cast<unsigned long long*>(w.sums) + (long long)bh * k * kD;
+  const int32_t* __restrict__ lab = w.labels + (long long)bh * N;
+  const uint32_t* __restrict__ V32 = reinterpret_cast<const uint32_t*>(V + (long long)bh * N * kD);
+  constexpr int kPerWave = kAccTok / (kAccThreads / 64);
+  constexpr int kBatch = 16;
+  const long long j_begin = (long long)blockIdx.x * kAccTok + (long long)wv * kPerWave;
+#pragma unroll 1
+  for (int j0 = 0; j0 < kPerWave; j0 += kBatch) {
+    if (j_begin + j0 >= N) break;
+    uint32_t raw[kBatch];
+    int cl[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const long long j = j_begin + j0 + b;
+      const long long jj = j < N ? j : (long long)N - 1;
+      cl[b] = j < N ? lab[jj] : -1;   // uniform address: a scalar load
+      raw[b] = V32[jj * (kD / 2) + ln];
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (cl[b] < 0) continue;   // beyond N (uniform across the wavefront)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float xv = __uint_as_float(h ? (raw[b] & 0xFFFF0000u) : (raw[b] << 16));
+        const long long qv = (long long)__builtin_rintf(xv * 16777216.0f);
+        if (kLdsSums) atomicAdd(&psum[cl[b] * kD + 64 * h + ln], (unsigned long long)qv);
+        else atomicAdd(&gs[(long long)cl[b] * kD + 2 * ln + h], (unsigned long long)qv);
+      }
+    }
+  }
   if (kLdsSums) {
-    unsigned long long* gs = reinterpret_cast<unsigned long long*>(w.sums) + (long long)bh * k * kD;
-    for (int idx = tid; idx < k * kD; idx += kAssignThreads)
-      if (psum[idx]) atomicAdd(&gs[idx], psum[idx]);
+    __syncthreads();
+    for (int idx = tid; idx < k * kD; idx += kAccThreads) {
+      const unsigned long long v = psum[idx];
+      const int c = idx / kD, slot = idx % kD;
+      if (v) atomicAdd(&gs[(long long)c * kD + 2 * (slot & 63) + (slot >> 6)], v);
+    }
   }
 }
 
@@ -294,23 +329,20 @@ extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, i
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int nchunks = (N + kSortChunk - 1) / kSortChunk;
   const bool lds_sums = k <= kLdsSumsMaxK;
-  const size_t lds = 8 * (size_t)((k + 1) / 2) + (lds_sums ? sizeof(unsigned long long) * (size_t)k * kD : 0);
+  const size_t lds = lds_sums ? sizeof(unsigned long long) * (size_t)k * kD : 0;
   const dim3 gA((N + kTokPerWG - 1) / kTokPerWG, (unsigned)BH);
-
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kmeans_assign<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kmeans_assign<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
+  const dim3 gS((N + kAccTok - 1) / kAccTok, (unsigned)BH);
+  // dynamic LDS above the default limit (cheap; set on every call, no state kept)
+  if (lds_sums)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kmeans_accum<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kmeans_init, dim3(k, (unsigned)BH), dim3(kD), 0, st, V, N, k, w);
   for (int it = 0; it < iters; ++it) {
+    hipLaunchKernelGGL(kmeans_assign, gA, dim3(kAssignThreads), 0, st, V, N, k, w);
     if (lds_sums)
-      hipLaunchKernelGGL(kmeans_assign<true>, gA, dim3(kAssignThreads), lds, st, V, N, k, w);
+      hipLaunchKernelGGL(kmeans_accum<true>, gS, dim3(kAccThreads), lds, st, V, N, k, w);
     else
-      hipLaunchKernelGGL(kmeans_assign<false>, gA, dim3(kAssignThreads), lds, st, V, N, k, w);
+      hipLaunchKernelGGL(kmeans_accum<false>, gS, dim3(kAccThreads), 0, st, V, N, k, w);
     hipLaunchKernelGGL(kmeans_update, dim3(k, (unsigned)BH), dim3(kD), 0, st, k, w);
   }
   hipLaunchKernelGGL(sort_hist, dim3(nchunks, (unsigned)BH), dim3(256), sizeof(unsigned) * k, st, N, k,
