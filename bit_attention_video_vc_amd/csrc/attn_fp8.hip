@@ -11,8 +11,9 @@
 // Restore) and "ExpCast-FP8".
 //
 // Design (MI355X-first, not the pages' Blackwell kernel):
-//  * one workgroup = 4 wavefronts = one 128-query block (one Q scale); every
-//    wavefront owns 32 queries and runs V_MFMA_F32_32X32X64_F8F6F4 (OCP E4M3).
+//  * one workgroup = 8 wavefronts = two 128-query blocks (one Q scale each)
+//    sharing every K/V tile copy; every wavefront owns 32 queries and runs
+//    V_MFMA_F32_32X32X64_F8F6F4 (OCP E4M3).
 //  * scores are computed transposed, S^T = K . Q^T (K rows are the MFMA rows),
 //    so each lane holds the scores of ONE query.  Row max needs one cross-lane
 //    step, and the ExpCast bytes land directly in the lane layout of the
@@ -21,11 +22,15 @@
 //    consecutive keys, matching 32 consecutive bytes of the transposed V block.
 //  * K and V^T tiles (16 KiB each) are double-buffered in LDS with an XOR chunk
 //    swizzle that keeps the 128-bit operand reads free of bank conflicts.
-//  * the row sum of the decoded P bytes comes from one extra MFMA against an
-//    all-ones operand (exact: every E4M3 value is a multiple of 2^-9), and the
+//  * the row sum of the decoded P bytes comes from a 16x16x128 FP8 MFMA against
+//    a ones pattern (exact: every E4M3 value is a multiple of 2^-9), and the
 //    block mean is restored as U += rowsum (x) mean_t / sv with a rank-2 fp32
 //    MFMA per two KV blocks, so no VALU instruction touches the accumulators
 //    except the (rare) rescale when a running max moves.
+//  * tiles are copied global -> LDS through buffer resources; the Q block scale
+//    is scalar and the next K block scale is prefetched with its copy, so no
+//    wait for a copy sits inside a tile; the row max crosses the two 32-lane
+//    halves with V_PERMLANE32_SWAP (no LDS).
 //  * workgroups are ordered head-major and handed to the 8 XCDs in contiguous
 //    ranges, so the workgroups sharing an XCD's L2 stream the same K/V blocks.
 #include <type_traits>
@@ -34,7 +39,7 @@
 
 namespace vc {
 
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 512;   // 8 wavefronts: two 128-query blocks sharing each K/V tile
 constexpr int kTile = kBlock * kD;   // bytes of one K or V^T tile
 
 struct AttnArgs {
@@ -63,8 +68,9 @@ __device__ __forceinline__ float max_across_halves(float x) {
   return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
-// MFMA bursts run at raised wave priority: the SIMD's other wavefront is then
-// usually in its VALU phase, and the arbiter interleaves the two.
+// MFMA bursts run at raised wave priority, so a wavefront's MFMAs are issued
+// as soon as the matrix unit frees up while the SIMD's other wavefront runs VALU
+// work.
 __device__ __forceinline__ void mfma_phase_begin() {
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(1);
@@ -77,7 +83,7 @@ __device__ __forceinline__ void mfma_phase_end() {
 }
 
 template <int kPMode, bool kDump>
-__global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(AttnArgs a) {
+__global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   // The two buffers of each operand are separate LDS objects so that reads of
   // one are not ordered behind the asynchronous copies into the other (the
   // copies are tracked by the vector memory counter).
@@ -89,11 +95,15 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
   __shared__ float InvSv[kD];
   __shared__ float Sv[kD];
 
-  const int nqb = a.nb;
-  const int item = xcd_item(blockIdx.x, nqb * a.BH);
-  const int bh = item / nqb, qb = item % nqb;
+  const int npair = (a.nb + 1) >> 1;
+  const int item = xcd_item(blockIdx.x, npair * a.BH);
+  const int bh = item / npair, pr = item % npair;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
+  // wavefronts 4w..4w+3 take query block 2*pr + w; when nb is odd the last
+  // pair's second block does not exist: it repeats the first and stores nothing
+  const bool qvalid = 2 * pr + (wave >> 2) < a.nb;
+  const int qb = qvalid ? 2 * pr + (wave >> 2) : 2 * pr;
   const int g = lane >> 5, col = lane & 31;
   const int N = a.N, nb = a.nb;
   const long long Np = (long long)nb * kBlock;
@@ -106,7 +116,7 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
   }
 
   // Q operand (B of S^T = K.Q^T): query row, 32 bytes per channel half.
-  const int qrow = qb * kBlock + wave * 32 + col;
+  const int qrow = qb * kBlock + (wave & 3) * 32 + col;
   v8i qop[2];
   {
     const uint8_t* qp = a.q + ((long long)bh * Np + qrow) * kD;
@@ -139,24 +149,20 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
   float ksn = 0.0f;   // K scale of the block in flight; becomes the next block's
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)nb * kTile);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)nb * kTile);
-  uint32_t dkoff[2], dvoff;
+  uint32_t dkoff, dvoff;   // copy j = wave + 8i: rows of i = 0, 1 differ by 64 (neither swizzle changes)
   {
     const int pos = lane & 7;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = 8 * (4 * i + wave) + (lane >> 3);
-      dkoff[i] = (uint32_t)(row * kD + 16 * (pos ^ swz_k(row)));
-    }
     const int row = 8 * wave + (lane >> 3);
+    dkoff = (uint32_t)(row * kD + 16 * (pos ^ swz_k(row)));
     dvoff = (uint32_t)(row * kD + 16 * (pos ^ swz_v(row)));
   }
   auto load_tile = [&](int t, int buf) {
     const uint32_t toff = (uint32_t)t * kTile;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * i + wave;
-      dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * j, dkoff[i & 1], toff + 8192u * (i >> 1));
-      dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * j, dvoff, toff + 4096u * i);
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave + 8 * i;
+      dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * j, dkoff, toff + 8192u * i);
+      dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * j, dvoff, toff + 8192u * i);
     }
     if (tid < kD) mr = mbase[(long long)t * kD + tid];
     ksn = a.ks[(long long)bh * nb + t];   // K scale of the block being copied
@@ -296,7 +302,7 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
         }
     }
 
-    if (kDump && qrow < N) {
+    if (kDump && qvalid && qrow < N) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -369,7 +375,7 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
   if (t < nb) step(t, std::integral_constant<int, 0>{});
 
   // ---- epilogue: O = sv * U / l, original query order ----
-  if (qrow < N) {
+  if (qvalid && qrow < N) {
     const float invl = 1.0f / l;
     float* op = a.out + ((long long)bh * N + qrow) * kD;
 #pragma unroll
@@ -388,7 +394,7 @@ __global__ void __launch_bounds__(kAttnThreads, kDump ? 1 : 2) attn_fp8_e4m3(Att
 }
 
 static int launch_e4m3(const AttnArgs& a, int p_mode, bool dump, hipStream_t st) {
-  const dim3 grid((unsigned)(a.nb * a.BH));
+  const dim3 grid((unsigned)(((a.nb + 1) / 2) * a.BH));   // one workgroup per pair of query blocks
   const dim3 block(kAttnThreads);
   if (p_mode == VC_P_EXPCAST) {
     if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, true>), grid, block, 0, st, a);
