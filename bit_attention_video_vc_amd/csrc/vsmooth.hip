@@ -30,6 +30,9 @@ constexpr int kAssignThreads = 256;
 constexpr int kTokPerThread = 2;
 constexpr int kTokPerWG = kAssignThreads * kTokPerThread;  // 512 tokens
 constexpr int kAccThreads = 256;
+constexpr int kMTokWG = 1024;                              // tokens per screened-assignment workgroup
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int kAccTok = 2048;                              // tokens per accumulation workgroup
 constexpr int kLdsSumsMaxK = 64;                           // LDS partial sums up to k = 64
 constexpr int kSortChunk = 1024;
@@ -37,6 +40,8 @@ constexpr int kSortChunk = 1024;
 struct KmWork {
   float* cent;     // [BH, k, 128]
   float* cc;       // [BH, k]
+  int8_t* cq;      // [BH, k, 2, 128] two int8 digits of every centroid value (screening pass)
+  float4* ctab;    // [BH, k] {code scale, L1 norm bound, max |c|, 0} (screening pass)
   long long* sums; // [BH, k, 128]
   unsigned* counts;// [BH, k]
   int32_t* labels; // [BH, N]
@@ -49,6 +54,49 @@ __device__ float centroid_norm(const float* c) {
   for (int i = 0; i < kD; ++i) acc = __builtin_fmaf(c[i], c[i], acc);
   return acc;
 }
+
+// Two int8 digits of a value x of a row with scale s = max|row| / 127:
+// h = RNE(x / s) (|h| <= 127), then l = RNE((x - h s) / (s / 254)) (|l| <= 127),
+// so |x - (h s + l s / 254)| <= (s / 254) (1/2 + 2^-14).
+__device__ __forceinline__ void two_digits(float x, float s, float inv_s, int& h, int& l) {
+  const float hf = fminf(fmaxf(__builtin_rintf(x * inv_s), -127.0f), 127.0f);
+  const float e = __builtin_fmaf(-hf, s, x);
+  const float lf = fminf(fmaxf(__builtin_rintf(e * (254.0f * inv_s)), -127.0f), 127.0f);
+  h = (int)hf;
+  l = (int)lf;
+}
+
+// Screening data of one centroid (128 threads, row[] in LDS): two int8 digits of
+// every value, the scale s = max|c| / 127, an upper bound of the L1 norm and the
+// max norm.
+__device__ void centroid_codes(const float* row, int i, int8_t* cq, float4* ctab) {
+  __shared__ float red[2][kD];
+  red[0][i] = fabsf(row[i]);
+  red[1][i] = fabsf(row[i]);
+  __syncthreads();
+  for (int o = kD / 2; o > 0; o >>= 1) {
+    if (i < o) {
+      red[0][i] = fmaxf(red[0][i], red[0][i + o]);
+      red[1][i] = red[1][i] + red[1][i + o];
+    }
+    __syncthreads();
+  }
+  const float cmax = red[0][0];
+  const float sc = cmax / 127.0f;
+  const float inv = cmax > 0.0f ? 1.0f / sc : 0.0f;
+  int h, l;
+  two_digits(row[i], sc, inv, h, l);
+  cq[i] = (int8_t)h;
+  cq[kD + i] = (int8_t)l;
+  // rows whose max lies outside [2^-40, 2^40] (and is not 0) are never screened
+  // out: far from fp32's normal range the rounding terms of the bound no longer hold
+  const bool screenable = cmax == 0.0f || (cmax >= 0x1p-40f && cmax <= 0x1p40f);
+  if (i == 0) *ctab = make_float4(sc, red[1][0] * (1.0f + 0x1p-15f), cmax, screenable ? 0.0f : 1.0f);
+}
+
+// value of lane l ^ 32
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+__device__ __forceinline__ int swap_halves(int x) { return __shfl_xor(x, 32); }
 
 __global__ void __launch_bounds__(kD) kmeans_init(const uint16_t* __restrict__ V, int N, int k,
                                                   KmWork w) {
@@ -65,6 +113,7 @@ __global__ void __launch_bounds__(kD) kmeans_init(const uint16_t* __restrict__ V
     w.cc[(long long)bh * k + c] = centroid_norm(row);
     w.counts[(long long)bh * k + c] = 0u;
   }
+  centroid_codes(row, i, w.cq + ((long long)bh * k + c) * 2 * kD, w.ctab + (long long)bh * k + c);
 }
 
 __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* __restrict__ V, int N, int k,
@@ -129,6 +178,213 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* 
     }
     w.labels[(long long)bh * N + j] = best;
     atomicAdd(&cnt[best], 1u);
+  }
+  __syncthreads();
+  for (int c = tid; c < k; c += kAssignThreads)
+    if (cnt[c]) atomicAdd(&w.counts[(long long)bh * k + c], cnt[c]);
+}
+
+// Screened assignment (k <= 64).  The distance of the fixed-order fp32 rule is
+// the arbiter; a screen finds every token whose argmin it decides.
+//  * The token's bf16 values and every centroid are coded as two int8 digits
+//    with one scale s per row: x ~ s h + (s / 254) l, error <= (s / 254)
+//    (1/2 + 2^-14).  V_MFMA_I32_32X32X32_I8 gives the exact integer dot
+//    products D_hh of the high digits and D_x = D_hl + D_lh of the mixed ones
+//    (both carry the scale s_v s_c / 254); the low-low term is dropped.
+//  * The screened score s_a = fmaf(-2, s_v s_c (D_hh + D_x / 254), cc) differs
+//    from the fixed-order score s_o by at most
+//    B = (s_c |v|_1 + s_v |c|_1) / 254 (digit errors, times 2)
+//      + 2 * 128 * 127^2 s_v s_c / 254^2 (the dropped low-low term, times 2)
+//      + 2^-15 |v|_1 max|c| (the fp32 chain) + rounding terms,
+//    inflated for the evaluation of B itself.
+//  * With U = min_c (s_a + B), only centroids with s_a - B <= U can be the
+//    argmin.  One such centroid is the fixed-order argmin (all others score
+//    strictly more).  Otherwise the token is recomputed with the fixed-order
+//    chain itself: lane c takes centroid c, the lowest index wins ties.  So is
+//    every token, and every centroid counts as a candidate, whose max |x| lies
+//    outside [2^-40, 2^40] (0 aside), where the rounding terms would not hold.
+//  * Per centroid, B = A_c |v|_1 + s_v B_c + 2^-18 |d_a| + 2^-19 |cc| with
+//    A_c = 1.002 (s_c / 254 + 2^-15 max|c|) and B_c = 1.002 (|c|_1 / 254 +
+//    64.02 s_c) taken from an LDS table.
+//  * Token digits are rounded to bytes q + 128 by V_CVT_PK_U8_F32 (round to
+//    nearest even, as RNE(x / s) is) and turned back to int8 by one XOR per word.
+// Lane layout: lanes l and l + 32 share token l % 32 (channel halves of each
+// 32-channel slice: the B operand of the MFMA); the output rows (centroids)
+// 8(r/4) + 4(l/32) + r%4 of each 32-centroid block stay in lane l.
+__global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint16_t* __restrict__ V, int N, int k,
+                                                                      KmWork w) {
+  __shared__ float Ct[kD][kLdsSumsMaxK];   // centroids transposed, for the fixed-order recheck
+  // centroid digits as MFMA A operands: [digit][slice][half][centroid][16 bytes]
+  __shared__ __align__(16) uint4 cqs[2][4][2][kLdsSumsMaxK];
+  __shared__ float4 tabA[kLdsSumsMaxK];    // {s_c, A_c, B_c, cc} of the bound (below)
+  __shared__ float tabC[kLdsSumsMaxK];     // 2^-19 |cc|
+  __shared__ float ccs[kLdsSumsMaxK];
+  __shared__ unsigned cnt[kLdsSumsMaxK];
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, g = lane >> 5, col = lane & 31;
+  const float* __restrict__ C = w.cent + (long long)bh * k * kD;
+  for (int idx = tid; idx < k * kD; idx += kAssignThreads) Ct[idx % kD][idx / kD] = C[idx];
+  for (int c = tid; c < k; c += kAssignThreads) {
+    const float4 t = w.ctab[(long long)bh * k + c];   // {s_c, |c|_1 bound, max|c|, 0}
+    const float cc = w.cc[(long long)bh * k + c];
+    // B = A_c |v|_1 + s_v B_c + 2^-19 |cc| + 2^-18 |da|, with the 1.002 inflation
+    tabA[c] = make_float4(t.x, 1.002f * (t.x * (1.0f / 254.0f) + 0x1p-15f * t.z),
+                          1.002f * (t.y * (1.0f / 254.0f) + 64.02f * t.x), cc);
+    tabC[c] = t.w == 0.0f ? 0x1p-19f * fabsf(cc) : __builtin_inff();   // infinite bound: always a candidate
+    ccs[c] = cc;
+    cnt[c] = 0u;
+  }
+  for (int idx = tid; idx < 2 * 4 * 2 * kLdsSumsMaxK; idx += kAssignThreads) {
+    const int c = idx % kLdsSumsMaxK, gg = (idx / kLdsSumsMaxK) % 2, s4 = (idx / (2 * kLdsSumsMaxK)) % 4,
+              dg = idx / (8 * kLdsSumsMaxK);
+    cqs[dg][s4][gg][c] = c < k ? *reinterpret_cast<const uint4*>(w.cq + (((long long)bh * k + c) * 2 + dg) * kD +
+                                                                  32 * s4 + 16 * gg)
+                               : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const int nblk = (k + 31) >> 5;
+  __syncthreads();
+
+  const int wave = tid >> 6;
+  const long long wbase = (long long)blockIdx.x * kMTokWG + (long long)wave * (kMTokWG / 4);
+#pragma unroll 1
+  for (int grp = 0; grp < kMTokWG / 4 / 32; ++grp) {
+    const long long t0 = wbase + 32 * grp;
+    if (t0 >= N) break;
+    const long long t = t0 + col;
+    const bool live = t < N;
+    const uint16_t* vp = V + ((long long)bh * N + (live ? t : t0)) * kD;
+    // this lane's 64 channels: 32 s + 16 g + e, s = 0..3, e = 0..15 (bf16 pairs)
+    uint32_t raw[4][8];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 u = *reinterpret_cast<const uint4*>(vp + 32 * s4 + 16 * g + 8 * h);
+        raw[s4][4 * h + 0] = u.x; raw[s4][4 * h + 1] = u.y; raw[s4][4 * h + 2] = u.z; raw[s4][4 * h + 3] = u.w;
+      }
+    // max |v| from the magnitude bits (they order like the values), |v|_1 bound
+    uint32_t mb = 0u;
+    float l1 = 0.0f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t wd = raw[s4][q];
+        mb = max(mb, max(wd & 0x7FFFu, (wd >> 16) & 0x7FFFu));
+        l1 += fabsf(__uint_as_float(wd << 16)) + fabsf(__uint_as_float(wd & 0xFFFF0000u));
+      }
+    const float vmax = fmaxf(__uint_as_float(mb << 16), swap_halves(__uint_as_float(mb << 16)));
+    l1 = (l1 + swap_halves(l1)) * (1.0f + 0x1p-15f);
+    const bool screenable = vmax == 0.0f || (vmax >= 0x1p-40f && vmax <= 0x1p40f);
+    const float sv = vmax / 127.0f;
+    const float inv = vmax > 0.0f ? 1.0f / sv : 0.0f;
+    const float inv254 = 254.0f * inv;
+    // Token digits, written as bytes b = q + 128 by V_CVT_PK_U8_F32 and turned
+    // into int8 by one XOR per word: h = RNE(x / s) exactly (h + 128 is an exact
+    // integer), l = RNE(fl(e * 254/s + 128)) - 128 with e = fl(x - h s); both stay
+    // within [-127, 127] because |x / s| <= 127, and |x - h s - l s / 254| <=
+    // (s / 254) (1/2 + 2^-14).
+    v4i bop[2][4];   // [high/low][slice]
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint32_t wh = 0u, wl = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ee = 4 * q4 + e;
+          const uint32_t wd = raw[s4][ee >> 1];
+          const float x = __uint_as_float((ee & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+          const float qh = __builtin_rintf(x * inv);
+          const float r = __builtin_fmaf(-qh, sv, x);
+          wh = __builtin_amdgcn_cvt_pk_u8_f32(qh + 128.0f, e, wh);
+          wl = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(r, inv254, 128.0f), e, wl);
+        }
+        bop[0][s4][q4] = (int)(wh ^ 0x80808080u);
+        bop[1][s4][q4] = (int)(wl ^ 0x80808080u);
+      }
+    v16i acc[2], accx[2];   // D_hh and D_hl + D_lh per 32-centroid block
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[b][r] = accx[b][r] = 0;
+      if (b < nblk) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const uint4 ah = cqs[0][s4][g][32 * b + col], al = cqs[1][s4][g][32 * b + col];
+          const v4i aoh = {(int)ah.x, (int)ah.y, (int)ah.z, (int)ah.w};
+          const v4i aol = {(int)al.x, (int)al.y, (int)al.z, (int)al.w};
+          acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aoh, bop[0][s4], acc[b], 0, 0, 0);
+          accx[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aol, bop[0][s4], accx[b], 0, 0, 0);
+          accx[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aoh, bop[1][s4], accx[b], 0, 0, 0);
+        }
+      }
+    }
+    // pass 1: screened score s_a and bound B of centroid 32b + 8(r/4) + 4g + r%4;
+    // keep s_a - B, and U = min (s_a + B) over the token's centroids
+    float lo[2][16];
+    float U = __builtin_inff();
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (c < k) {
+          const float4 ta = tabA[c];
+          const float dint = __builtin_fmaf((float)accx[b][r], 1.0f / 254.0f, (float)acc[b][r]);
+          const float da = dint * (sv * ta.x);
+          const float sa = __builtin_fmaf(-2.0f, da, ta.w);
+          const float bd = __builtin_fmaf(ta.y, l1, __builtin_fmaf(sv, ta.z, __builtin_fmaf(0x1p-18f, fabsf(da), tabC[c])));
+          lo[b][r] = sa - bd;
+          U = fminf(U, sa + bd);
+        } else {
+          lo[b][r] = __builtin_inff();
+        }
+      }
+    U = fminf(U, swap_halves(U));
+    // pass 2: centroids that can still be the argmin
+    int ncand = 0, cand = -1;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (lo[b][r] <= U) {
+          ++ncand;
+          cand = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
+        }
+    ncand += swap_halves(ncand);
+    cand = max(cand, swap_halves(cand));
+    int label = cand;
+    // fixed-order recheck of the tokens the screen leaves open
+    unsigned long long open = __ballot(live && (ncand != 1 || !screenable) && g == 0);
+    while (open) {
+      const int tl = __builtin_ctzll(open);
+      open &= open - 1;
+      const uint16_t* tp = V + ((long long)bh * N + t0 + tl) * kD;
+      float d = 0.0f;
+      const int c = lane;
+#pragma unroll 8
+      for (int i = 0; i < kD; ++i) {   // fixed order: channel 0..127
+        const float xi = bf16_bits_to_f32(tp[i]);
+        d = __builtin_fmaf(xi, c < k ? Ct[i][c] : 0.0f, d);
+      }
+      float sc = c < k ? __builtin_fmaf(-2.0f, d, ccs[c]) : __builtin_inff();
+      int bi = c;
+      // argmin over the lanes, lowest index on ties
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float so = __shfl_xor(sc, o);
+        const int io = __shfl_xor(bi, o);
+        if (so < sc || (so == sc && io < bi)) {
+          sc = so;
+          bi = io;
+        }
+      }
+      if (col == tl) label = min(max(bi, 0), k - 1);   // in range even for non-finite data
+    }
+    if (live && g == 0) {
+      w.labels[(long long)bh * N + t] = label;
+      atomicAdd(&cnt[label], 1u);
+    }
   }
   __syncthreads();
   for (int c = tid; c < k; c += kAssignThreads)
@@ -207,6 +463,7 @@ __global__ void __launch_bounds__(kD) kmeans_update(int k, KmWork w) {
     w.cc[(long long)bh * k + c] = centroid_norm(row);
     w.counts[(long long)bh * k + c] = 0u;
   }
+  centroid_codes(row, i, w.cq + ((long long)bh * k + c) * 2 * kD, w.ctab + (long long)bh * k + c);
 }
 
 __global__ void __launch_bounds__(256) sort_hist(int N, int k, int nchunks, KmWork w) {
@@ -283,7 +540,7 @@ __global__ void __launch_bounds__(256) sort_scatter(int N, int k, int nchunks, K
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct KmLayout {
-  size_t cent, cc, sums, counts, labels, hist, total;
+  size_t cent, cc, cq, ctab, sums, counts, labels, hist, total;
 };
 
 static KmLayout km_layout(long long BH, long long N, int k) {
@@ -292,6 +549,8 @@ static KmLayout km_layout(long long BH, long long N, int k) {
   size_t o = 0;
   L.cent = o;   o += align256(sizeof(float) * BH * k * kD);
   L.cc = o;     o += align256(sizeof(float) * BH * k);
+  L.cq = o;     o += align256(sizeof(int8_t) * BH * k * 2 * kD);
+  L.ctab = o;   o += align256(sizeof(float4) * BH * k);
   L.sums = o;   o += align256(sizeof(long long) * BH * k * kD);
   L.counts = o; o += align256(sizeof(unsigned) * BH * k);
   L.labels = o; o += align256(sizeof(int32_t) * BH * N);
@@ -322,6 +581,8 @@ extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, i
   KmWork w;
   w.cent = centroids ? centroids : reinterpret_cast<float*>(ws + L.cent);
   w.cc = reinterpret_cast<float*>(ws + L.cc);
+  w.cq = reinterpret_cast<int8_t*>(ws + L.cq);
+  w.ctab = reinterpret_cast<float4*>(ws + L.ctab);
   w.sums = reinterpret_cast<long long*>(ws + L.sums);
   w.counts = reinterpret_cast<unsigned*>(ws + L.counts);
   w.labels = labels ? labels : reinterpret_cast<int32_t*>(ws + L.labels);
@@ -337,8 +598,12 @@ extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, i
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kmeans_accum<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kmeans_init, dim3(k, (unsigned)BH), dim3(kD), 0, st, V, N, k, w);
+  const dim3 gM((N + kMTokWG - 1) / kMTokWG, (unsigned)BH);
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL(kmeans_assign, gA, dim3(kAssignThreads), 0, st, V, N, k, w);
+    if (k <= kLdsSumsMaxK)   // screened int8 MFMA pass with a fixed-order recheck
+      hipLaunchKernelGGL(kmeans_assign_mfma, gM, dim3(kAssignThreads), 0, st, V, N, k, w);
+    else
+      hipLaunchKernelGGL(kmeans_assign, gA, dim3(kAssignThreads), 0, st, V, N, k, w);
     if (lds_sums)
       hipLaunchKernelGGL(kmeans_accum<true>, gS, dim3(kAccThreads), lds, st, V, N, k, w);
     else
