@@ -21,13 +21,18 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
          "-Wno-unused-result", "-I", os.path.join(HERE, "..", "include")]
 
 
+# per-source extra flags: the screened k-means keeps its MFMA accumulators in
+# VGPRs (no AGPR copies, one more wavefront per SIMD)
+EXTRA = {"vsmooth.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-I",
                os.path.join(HERE, "..", "include"), "-c", os.path.join(CSRC, src), "-o", obj]

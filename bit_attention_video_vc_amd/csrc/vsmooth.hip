@@ -29,19 +29,19 @@ namespace vc {
 constexpr int kAssignThreads = 256;
 constexpr int kTokPerThread = 2;
 constexpr int kTokPerWG = kAssignThreads * kTokPerThread;  // 512 tokens
-constexpr int kAccThreads = 256;
-constexpr int kMTokWG = 1024;                              // tokens per screened-assignment workgroup
+constexpr int kAccThreads = 512;
+constexpr int kMTokWG = 2048;                              // tokens per screened-assignment workgroup
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-constexpr int kAccTok = 2048;                              // tokens per accumulation workgroup
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr int kAccTok = 4096;                              // tokens per accumulation workgroup
 constexpr int kLdsSumsMaxK = 64;                           // LDS partial sums up to k = 64
 constexpr int kSortChunk = 1024;
 
 struct KmWork {
   float* cent;     // [BH, k, 128]
   float* cc;       // [BH, k]
-  int8_t* cq;      // [BH, k, 2, 128] two int8 digits of every centroid value (screening pass)
-  float4* ctab;    // [BH, k] {code scale, L1 norm bound, max |c|, 0} (screening pass)
   long long* sums; // [BH, k, 128]
   unsigned* counts;// [BH, k]
   int32_t* labels; // [BH, N]
@@ -66,34 +66,6 @@ __device__ __forceinline__ void two_digits(float x, float s, float inv_s, int& h
   l = (int)lf;
 }
 
-// Screening data of one centroid (128 threads, row[] in LDS): two int8 digits of
-// every value, the scale s = max|c| / 127, an upper bound of the L1 norm and the
-// max norm.
-__device__ void centroid_codes(const float* row, int i, int8_t* cq, float4* ctab) {
-  __shared__ float red[2][kD];
-  red[0][i] = fabsf(row[i]);
-  red[1][i] = fabsf(row[i]);
-  __syncthreads();
-  for (int o = kD / 2; o > 0; o >>= 1) {
-    if (i < o) {
-      red[0][i] = fmaxf(red[0][i], red[0][i + o]);
-      red[1][i] = red[1][i] + red[1][i + o];
-    }
-    __syncthreads();
-  }
-  const float cmax = red[0][0];
-  const float sc = cmax / 127.0f;
-  const float inv = cmax > 0.0f ? 1.0f / sc : 0.0f;
-  int h, l;
-  two_digits(row[i], sc, inv, h, l);
-  cq[i] = (int8_t)h;
-  cq[kD + i] = (int8_t)l;
-  // rows whose max lies outside [2^-40, 2^40] (and is not 0) are never screened
-  // out: far from fp32's normal range the rounding terms of the bound no longer hold
-  const bool screenable = cmax == 0.0f || (cmax >= 0x1p-40f && cmax <= 0x1p40f);
-  if (i == 0) *ctab = make_float4(sc, red[1][0] * (1.0f + 0x1p-15f), cmax, screenable ? 0.0f : 1.0f);
-}
-
 // value of lane l ^ 32
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 __device__ __forceinline__ int swap_halves(int x) { return __shfl_xor(x, 32); }
@@ -113,7 +85,6 @@ __global__ void __launch_bounds__(kD) kmeans_init(const uint16_t* __restrict__ V
     w.cc[(long long)bh * k + c] = centroid_norm(row);
     w.counts[(long long)bh * k + c] = 0u;
   }
-  centroid_codes(row, i, w.cq + ((long long)bh * k + c) * 2 * kD, w.ctab + (long long)bh * k + c);
 }
 
 __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* __restrict__ V, int N, int k,
@@ -187,73 +158,108 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* 
 // Screened assignment (k <= 64).  The distance of the fixed-order fp32 rule is
 // the arbiter; a screen finds every token whose argmin it decides.
 //  * The token's bf16 values and every centroid are coded as two int8 digits
-//    with one scale s per row: x ~ s h + (s / 254) l, error <= (s / 254)
-//    (1/2 + 2^-14).  V_MFMA_I32_32X32X32_I8 gives the exact integer dot
-//    products D_hh of the high digits and D_x = D_hl + D_lh of the mixed ones
-//    (both carry the scale s_v s_c / 254); the low-low term is dropped.
-//  * The screened score s_a = fmaf(-2, s_v s_c (D_hh + D_x / 254), cc) differs
+//    with one scale s per row (s = max|row| / 127): x ~ s h + (s / 254) l,
+//    error <= (s / 254) (1/2 + 2^-14).  V_MFMA_I32_32X32X32_I8 gives the exact
+//    integer dot products D_hh of the high digits and D_x = D_hl + D_lh of the
+//    mixed ones; the low-low term is dropped.
+//  * The screened score s_a = cc - 2 s_v s_c (254 D_hh + D_x) / 254 differs
 //    from the fixed-order score s_o by at most
-//    B = (s_c |v|_1 + s_v |c|_1) / 254 (digit errors, times 2)
-//      + 2 * 128 * 127^2 s_v s_c / 254^2 (the dropped low-low term, times 2)
-//      + 2^-15 |v|_1 max|c| (the fp32 chain) + rounding terms,
-//    inflated for the evaluation of B itself.
+//    B = 1.002 [ (s_c |v|_1 + s_v |c|_1) / 254      (digit errors, times 2)
+//              + 64.02 s_v s_c                      (dropped low-low term: 2 * 128 * 127^2 / 254^2)
+//              + (2^-15 + 2^-17) |v|_1 max|c| ]     (fp32 chain of s_o; rounding of s_a)
+//        + 2^-19 |cc|                               (rounding of s_a and of the comparison)
+//    where the factor 1.002 covers the evaluation of B.  Per centroid, B =
+//    A_c |v|_1 + s_v B_c + C_c with A_c, B_c, C_c from an LDS table.
 //  * With U = min_c (s_a + B), only centroids with s_a - B <= U can be the
-//    argmin.  One such centroid is the fixed-order argmin (all others score
-//    strictly more).  Otherwise the token is recomputed with the fixed-order
+//    argmin.  A token with one such centroid takes it (all others score
+//    strictly more); any other token is recomputed with the fixed-order
 //    chain itself: lane c takes centroid c, the lowest index wins ties.  So is
 //    every token, and every centroid counts as a candidate, whose max |x| lies
 //    outside [2^-40, 2^40] (0 aside), where the rounding terms would not hold.
-//  * Per centroid, B = A_c |v|_1 + s_v B_c + 2^-18 |d_a| + 2^-19 |cc| with
-//    A_c = 1.002 (s_c / 254 + 2^-15 max|c|) and B_c = 1.002 (|c|_1 / 254 +
-//    64.02 s_c) taken from an LDS table.
-//  * Token digits are rounded to bytes q + 128 by V_CVT_PK_U8_F32 (round to
-//    nearest even, as RNE(x / s) is) and turned back to int8 by one XOR per word.
+//  * Token digits: the high one from the 1.5 * 2^23 rounding trick (its byte is
+//    the low byte of the sum), the low one rounded to a byte q + 128 by
+//    V_CVT_PK_U8_F32; one XOR per word turns bytes q + 128 into int8.
 // Lane layout: lanes l and l + 32 share token l % 32 (channel halves of each
 // 32-channel slice: the B operand of the MFMA); the output rows (centroids)
 // 8(r/4) + 4(l/32) + r%4 of each 32-centroid block stay in lane l.
 __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint16_t* __restrict__ V, int N, int k,
                                                                       KmWork w) {
-  __shared__ float Ct[kD][kLdsSumsMaxK];   // centroids transposed, for the fixed-order recheck
+  __shared__ float Ct[kD][kLdsSumsMaxK + 1];   // centroids transposed (zero past k), padded against bank conflicts
   // centroid digits as MFMA A operands: [digit][slice][half][centroid][16 bytes]
   __shared__ __align__(16) uint4 cqs[2][4][2][kLdsSumsMaxK];
-  __shared__ float4 tabA[kLdsSumsMaxK];    // {s_c, A_c, B_c, cc} of the bound (below)
-  __shared__ float tabC[kLdsSumsMaxK];     // 2^-19 |cc|
-  __shared__ float ccs[kLdsSumsMaxK];
+  __shared__ float ccs[kLdsSumsMaxK];      // |c|^2, +inf past k
+  __shared__ float part[2][4][kLdsSumsMaxK];
+  __shared__ float scs[kLdsSumsMaxK];      // s_c
+  __shared__ float4 tabA[kLdsSumsMaxK];    // {-2 s_c / 254, A_c, B_c, cc} (zero and +inf past k)
+  __shared__ float tabC[kLdsSumsMaxK];     // C_c
   __shared__ unsigned cnt[kLdsSumsMaxK];
   const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, g = lane >> 5, col = lane & 31;
   const float* __restrict__ C = w.cent + (long long)bh * k * kD;
-  for (int idx = tid; idx < k * kD; idx += kAssignThreads) Ct[idx % kD][idx / kD] = C[idx];
-  for (int c = tid; c < k; c += kAssignThreads) {
-    const float4 t = w.ctab[(long long)bh * k + c];   // {s_c, |c|_1 bound, max|c|, 0}
-    const float cc = w.cc[(long long)bh * k + c];
-    // B = A_c |v|_1 + s_v B_c + 2^-19 |cc| + 2^-18 |da|, with the 1.002 inflation
-    tabA[c] = make_float4(t.x, 1.002f * (t.x * (1.0f / 254.0f) + 0x1p-15f * t.z),
-                          1.002f * (t.y * (1.0f / 254.0f) + 64.02f * t.x), cc);
-    tabC[c] = t.w == 0.0f ? 0x1p-19f * fabsf(cc) : __builtin_inff();   // infinite bound: always a candidate
-    ccs[c] = cc;
-    cnt[c] = 0u;
+  for (int idx = tid; idx < kLdsSumsMaxK * kD; idx += kAssignThreads) {
+    const int c = idx / kD, i = idx % kD;
+    Ct[i][c] = c < k ? C[idx] : 0.0f;
   }
-  for (int idx = tid; idx < 2 * 4 * 2 * kLdsSumsMaxK; idx += kAssignThreads) {
-    const int c = idx % kLdsSumsMaxK, gg = (idx / kLdsSumsMaxK) % 2, s4 = (idx / (2 * kLdsSumsMaxK)) % 4,
-              dg = idx / (8 * kLdsSumsMaxK);
-    cqs[dg][s4][gg][c] = c < k ? *reinterpret_cast<const uint4*>(w.cq + (((long long)bh * k + c) * 2 + dg) * kD +
-                                                                  32 * s4 + 16 * gg)
-                               : make_uint4(0u, 0u, 0u, 0u);
+  if (tid < kLdsSumsMaxK) {
+    ccs[tid] = tid < k ? w.cc[(long long)bh * k + tid] : __builtin_inff();
+    cnt[tid] = 0u;
+  }
+  __syncthreads();
+  {  // per-centroid |c|_1 and max|c| over channel quarters
+    const int c = tid & 63, q = tid >> 6;
+    float l1 = 0.0f, mx = 0.0f;
+    for (int i = 32 * q; i < 32 * q + 32; ++i) {
+      l1 += fabsf(Ct[i][c]);
+      mx = fmaxf(mx, fabsf(Ct[i][c]));
+    }
+    part[0][q][c] = l1;
+    part[1][q][c] = mx;
+  }
+  __syncthreads();
+  if (tid < kLdsSumsMaxK) {
+    const int c = tid;
+    const float l1 = (((part[0][0][c] + part[0][1][c]) + part[0][2][c]) + part[0][3][c]) * (1.0f + 0x1p-15f);
+    const float mx = fmaxf(fmaxf(part[1][0][c], part[1][1][c]), fmaxf(part[1][2][c], part[1][3][c]));
+    const float sc = mx / 127.0f;
+    // a centroid outside the screened range is a candidate for every token
+    const bool ok = mx == 0.0f || (mx >= 0x1p-40f && mx <= 0x1p40f);
+    scs[c] = sc;
+    if (c < k) {
+      tabA[c] = make_float4((-2.0f / 254.0f) * sc, 1.002f * (sc * (1.0f / 254.0f) + (0x1p-15f + 0x1p-17f) * mx),
+                            1.002f * (l1 * (1.0f / 254.0f) + 64.02f * sc), ccs[c]);
+      tabC[c] = ok ? 0x1p-19f * fabsf(ccs[c]) : __builtin_inff();
+    } else {
+      tabA[c] = make_float4(0.0f, 0.0f, 0.0f, __builtin_inff());
+      tabC[c] = 0.0f;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 4 * 2 * kLdsSumsMaxK; idx += kAssignThreads) {
+    const int c = idx % kLdsSumsMaxK, gg = (idx / kLdsSumsMaxK) % 2, s4 = idx / (2 * kLdsSumsMaxK);
+    const float sc = scs[c], inv_c = sc > 0.0f ? 1.0f / sc : 0.0f;
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hw[q] = lw[q] = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int h, l;
+        two_digits(Ct[32 * s4 + 16 * gg + 4 * q + e][c], sc, inv_c, h, l);
+        hw[q] |= (uint32_t)(h & 0xFF) << (8 * e);
+        lw[q] |= (uint32_t)(l & 0xFF) << (8 * e);
+      }
+    }
+    cqs[0][s4][gg][c] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    cqs[1][s4][gg][c] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
   const int nblk = (k + 31) >> 5;
   __syncthreads();
 
   const int wave = tid >> 6;
   const long long wbase = (long long)blockIdx.x * kMTokWG + (long long)wave * (kMTokWG / 4);
-#pragma unroll 1
-  for (int grp = 0; grp < kMTokWG / 4 / 32; ++grp) {
-    const long long t0 = wbase + 32 * grp;
-    if (t0 >= N) break;
+  uint32_t raw[4][8];
+  auto load_group = [&](long long t0) {
     const long long t = t0 + col;
-    const bool live = t < N;
-    const uint16_t* vp = V + ((long long)bh * N + (live ? t : t0)) * kD;
-    // this lane's 64 channels: 32 s + 16 g + e, s = 0..3, e = 0..15 (bf16 pairs)
-    uint32_t raw[4][8];
+    const uint16_t* vp = V + ((long long)bh * N + (t < N ? t : t0)) * kD;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
@@ -261,96 +267,115 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
         const uint4 u = *reinterpret_cast<const uint4*>(vp + 32 * s4 + 16 * g + 8 * h);
         raw[s4][4 * h + 0] = u.x; raw[s4][4 * h + 1] = u.y; raw[s4][4 * h + 2] = u.z; raw[s4][4 * h + 3] = u.w;
       }
-    // max |v| from the magnitude bits (they order like the values), |v|_1 bound
-    uint32_t mb = 0u;
+  };
+  if (wbase < N) load_group(wbase);
+#pragma unroll 1
+  for (int grp = 0; grp < kMTokWG / 4 / 32; ++grp) {
+    const long long t0 = wbase + 32 * grp;
+    if (t0 >= N) break;
+    const long long t = t0 + col;
+    const bool live = t < N;
+    // max |v| from the magnitude bits (they order like the values, two at a time
+    // with V_PK_MAX_U16) and an upper bound of |v|_1 (V_DOT2_F32_BF16 against ones;
+    // its rounding and any flush of subnormals stay far inside the 2^-15 margin)
+    u16x2 mb = {0, 0};
     float l1 = 0.0f;
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const uint32_t wd = raw[s4][q];
-        mb = max(mb, max(wd & 0x7FFFu, (wd >> 16) & 0x7FFFu));
-        l1 += fabsf(__uint_as_float(wd << 16)) + fabsf(__uint_as_float(wd & 0xFFFF0000u));
+        const uint32_t mag = raw[s4][q] & 0x7FFF7FFFu;
+        mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, mag));
+        l1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, mag), ones, l1, false);
       }
-    const float vmax = fmaxf(__uint_as_float(mb << 16), swap_halves(__uint_as_float(mb << 16)));
+    const uint32_t mbw = __builtin_bit_cast(uint32_t, mb);
+    const float vmax_l = fmaxf(__uint_as_float(mbw << 16), __uint_as_float(mbw & 0xFFFF0000u));
+    const float vmax = fmaxf(vmax_l, swap_halves(vmax_l));
     l1 = (l1 + swap_halves(l1)) * (1.0f + 0x1p-15f);
     const bool screenable = vmax == 0.0f || (vmax >= 0x1p-40f && vmax <= 0x1p40f);
     const float sv = vmax / 127.0f;
     const float inv = vmax > 0.0f ? 1.0f / sv : 0.0f;
     const float inv254 = 254.0f * inv;
-    // Token digits, written as bytes b = q + 128 by V_CVT_PK_U8_F32 and turned
-    // into int8 by one XOR per word: h = RNE(x / s) exactly (h + 128 is an exact
-    // integer), l = RNE(fl(e * 254/s + 128)) - 128 with e = fl(x - h s); both stay
-    // within [-127, 127] because |x / s| <= 127, and |x - h s - l s / 254| <=
-    // (s / 254) (1/2 + 2^-14).
+    // Token digits.  High: t = fl(x / s + 1.5 * 2^23 + 128) rounds x / s to the
+    // nearest integer h (ties to even) in one step, t's low byte is h + 128 and
+    // t - (1.5 * 2^23 + 128) is h exactly.  Low: l = RNE(fl(e * 254/s + 128)) - 128
+    // with e = fl(x - h s), rounded to a byte by V_CVT_PK_U8_F32.  Both stay in
+    // [-127, 127] because |x / s| <= 127 (up to rounding), and |x - h s - l s / 254|
+    // <= (s / 254) (1/2 + 2^-14).  One XOR per word turns bytes q + 128 into int8.
+    constexpr float kMagic = 12583040.0f;   // 1.5 * 2^23 + 128
     v4i bop[2][4];   // [high/low][slice]
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        uint32_t wh = 0u, wl = 0u;
+        uint32_t tw[4];
+        uint32_t wl = 0u;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ee = 4 * q4 + e;
           const uint32_t wd = raw[s4][ee >> 1];
           const float x = __uint_as_float((ee & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
-          const float qh = __builtin_rintf(x * inv);
-          const float r = __builtin_fmaf(-qh, sv, x);
-          wh = __builtin_amdgcn_cvt_pk_u8_f32(qh + 128.0f, e, wh);
+          const float t = __builtin_fmaf(x, inv, kMagic);
+          const float r = __builtin_fmaf(-(t - kMagic), sv, x);
+          tw[e] = __float_as_uint(t);
           wl = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(r, inv254, 128.0f), e, wl);
         }
+        const uint32_t wh = __builtin_amdgcn_perm(tw[1], tw[0], 0x0C0C0400u) |
+                            __builtin_amdgcn_perm(tw[3], tw[2], 0x04000C0Cu);
         bop[0][s4][q4] = (int)(wh ^ 0x80808080u);
         bop[1][s4][q4] = (int)(wl ^ 0x80808080u);
       }
-    v16i acc[2], accx[2];   // D_hh and D_hl + D_lh per 32-centroid block
+    if (grp + 1 < kMTokWG / 4 / 32 && t0 + 32 < N) load_group(t0 + 32);
+    // screened scores s_a = cc - 2 s_v s_c D / 254 (D = 254 D_hh + D_x) of
+    // centroids 32b + 8(r/4) + 4g + r%4 (this lane's rows) with their bounds:
+    // keep s_a - B, and U = min (s_a + B) over the token's centroids
+    float lo[2][16];
+    float U = __builtin_inff();
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[b][r] = accx[b][r] = 0;
       if (b < nblk) {
+        v16i acc, accx;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = accx[r] = 0;
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const uint4 ah = cqs[0][s4][g][32 * b + col], al = cqs[1][s4][g][32 * b + col];
           const v4i aoh = {(int)ah.x, (int)ah.y, (int)ah.z, (int)ah.w};
           const v4i aol = {(int)al.x, (int)al.y, (int)al.z, (int)al.w};
-          acc[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aoh, bop[0][s4], acc[b], 0, 0, 0);
-          accx[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aol, bop[0][s4], accx[b], 0, 0, 0);
-          accx[b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aoh, bop[1][s4], accx[b], 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(aoh, bop[0][s4], acc, 0, 0, 0);
+          accx = __builtin_amdgcn_mfma_i32_32x32x32_i8(aol, bop[0][s4], accx, 0, 0, 0);
+          accx = __builtin_amdgcn_mfma_i32_32x32x32_i8(aoh, bop[1][s4], accx, 0, 0, 0);
         }
-      }
-    }
-    // pass 1: screened score s_a and bound B of centroid 32b + 8(r/4) + 4g + r%4;
-    // keep s_a - B, and U = min (s_a + B) over the token's centroids
-    float lo[2][16];
-    float U = __builtin_inff();
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (c < k) {
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
           const float4 ta = tabA[c];
-          const float dint = __builtin_fmaf((float)accx[b][r], 1.0f / 254.0f, (float)acc[b][r]);
-          const float da = dint * (sv * ta.x);
-          const float sa = __builtin_fmaf(-2.0f, da, ta.w);
-          const float bd = __builtin_fmaf(ta.y, l1, __builtin_fmaf(sv, ta.z, __builtin_fmaf(0x1p-18f, fabsf(da), tabC[c])));
+          // |254 D_hh + D_x| < 2^30: the 24-bit multiply-add is exact
+          const int di = __mul24(acc[r], 254) + accx[r];
+          const float sa = __builtin_fmaf((float)di, sv * ta.x, ta.w);
+          const float bd = __builtin_fmaf(ta.y, l1, __builtin_fmaf(ta.z, sv, tabC[c]));
           lo[b][r] = sa - bd;
           U = fminf(U, sa + bd);
-        } else {
-          lo[b][r] = __builtin_inff();
         }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lo[b][r] = __builtin_inff();
       }
+    }
     U = fminf(U, swap_halves(U));
-    // pass 2: centroids that can still be the argmin
+    // candidates: centroids that can still be the argmin (cand holds the row
+    // index without this lane's 4g)
     int ncand = 0, cand = -1;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (lo[b][r] <= U) {
-          ++ncand;
-          cand = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const bool in = lo[b][r] <= U;
+        ncand += in ? 1 : 0;
+        cand = in ? 32 * b + 8 * (r >> 2) + (r & 3) : cand;
+      }
+    cand = cand < 0 ? -1 : cand + 4 * g;
     ncand += swap_halves(ncand);
     cand = max(cand, swap_halves(cand));
     int label = cand;
@@ -382,6 +407,7 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
       if (col == tl) label = min(max(bi, 0), k - 1);   // in range even for non-finite data
     }
     if (live && g == 0) {
+      label = min(max(label, 0), k - 1);   // a lone candidate is always a real centroid; kept as a guard
       w.labels[(long long)bh * N + t] = label;
       atomicAdd(&cnt[label], 1u);
     }
@@ -463,7 +489,6 @@ __global__ void __launch_bounds__(kD) kmeans_update(int k, KmWork w) {
     w.cc[(long long)bh * k + c] = centroid_norm(row);
     w.counts[(long long)bh * k + c] = 0u;
   }
-  centroid_codes(row, i, w.cq + ((long long)bh * k + c) * 2 * kD, w.ctab + (long long)bh * k + c);
 }
 
 __global__ void __launch_bounds__(256) sort_hist(int N, int k, int nchunks, KmWork w) {
@@ -540,7 +565,7 @@ __global__ void __launch_bounds__(256) sort_scatter(int N, int k, int nchunks, K
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct KmLayout {
-  size_t cent, cc, cq, ctab, sums, counts, labels, hist, total;
+  size_t cent, cc, sums, counts, labels, hist, total;
 };
 
 static KmLayout km_layout(long long BH, long long N, int k) {
@@ -549,8 +574,6 @@ static KmLayout km_layout(long long BH, long long N, int k) {
   size_t o = 0;
   L.cent = o;   o += align256(sizeof(float) * BH * k * kD);
   L.cc = o;     o += align256(sizeof(float) * BH * k);
-  L.cq = o;     o += align256(sizeof(int8_t) * BH * k * 2 * kD);
-  L.ctab = o;   o += align256(sizeof(float4) * BH * k);
   L.sums = o;   o += align256(sizeof(long long) * BH * k * kD);
   L.counts = o; o += align256(sizeof(unsigned) * BH * k);
   L.labels = o; o += align256(sizeof(int32_t) * BH * N);
@@ -581,8 +604,6 @@ extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, i
   KmWork w;
   w.cent = centroids ? centroids : reinterpret_cast<float*>(ws + L.cent);
   w.cc = reinterpret_cast<float*>(ws + L.cc);
-  w.cq = reinterpret_cast<int8_t*>(ws + L.cq);
-  w.ctab = reinterpret_cast<float4*>(ws + L.ctab);
   w.sums = reinterpret_cast<long long*>(ws + L.sums);
   w.counts = reinterpret_cast<unsigned*>(ws + L.counts);
   w.labels = labels ? labels : reinterpret_cast<int32_t*>(ws + L.labels);
