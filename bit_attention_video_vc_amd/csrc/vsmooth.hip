@@ -534,31 +534,50 @@ __global__ void __launch_bounds__(256) sort_scan(int k, int nchunks, KmWork w) {
   }
 }
 
+// Stable scatter of one 1024-token chunk: wavefront w takes tokens 256w ..
+// 256w + 255 in steps of 64.  In a step, the lanes with the same label are
+// found by matching the label bits with ballots; a lane's rank is the count of
+// its label so far in the wavefront plus the matching lanes below it.  Ranks of
+// later wavefronts are offset by the counts of the earlier ones, so positions
+// follow the original token order within every label.
 __global__ void __launch_bounds__(256) sort_scatter(int N, int k, int nchunks, KmWork w,
                                                     int32_t* __restrict__ perm) {
-  __shared__ int lab[kSortChunk];
-  const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  static_assert(kSortChunk == 4 * 256, "four wavefronts of 256 tokens");
+  __shared__ int wcnt[4][256];   // per-wavefront label counts (k <= 256)
+  const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const long long base = (long long)chunk * kSortChunk;
   const int len = (int)min((long long)kSortChunk, (long long)N - base);
-  for (int q = tid; q < kSortChunk; q += 256) lab[q] = q < len ? w.labels[(long long)bh * N + base + q] : -1;
+  for (int q = tid; q < 4 * 256; q += 256) (&wcnt[0][0])[q] = 0;
   __syncthreads();
-  int mine[kSortChunk / 256], rank[kSortChunk / 256];
+  const int nbits = k <= 1 ? 0 : 32 - __clz(k - 1);
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int lbl[4], rank[4];
 #pragma unroll
-  for (int s = 0; s < kSortChunk / 256; ++s) {
-    mine[s] = lab[tid + s * 256];
-    rank[s] = 0;
+  for (int s = 0; s < 4; ++s) {
+    const int j = wave * 256 + s * 64 + lane;
+    const bool valid = j < len;
+    const int label = valid ? w.labels[(long long)bh * N + base + j] : 0;
+    unsigned long long match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (label >> b) & 1;
+      const unsigned long long bal = __ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    lbl[s] = label;
+    rank[s] = valid ? wcnt[wave][label] + __popcll(match & below) : 0;
+    // the highest lane of each label group adds the group's size
+    if (valid && (match >> lane) == 1ull) wcnt[wave][label] += __popcll(match);
   }
-  // rank = number of earlier tokens of the chunk with the same label (stable order)
-  for (int q = 0; q < len; ++q) {
-    const int lq = lab[q];
-#pragma unroll
-    for (int s = 0; s < kSortChunk / 256; ++s) rank[s] += (lq == mine[s] && q < tid + s * 256) ? 1 : 0;
-  }
+  __syncthreads();
   const int32_t* off = w.hist + ((long long)bh * nchunks + chunk) * k;
 #pragma unroll
-  for (int s = 0; s < kSortChunk / 256; ++s) {
-    const int j = tid + s * 256;
-    if (j < len) perm[(long long)bh * N + off[mine[s]] + rank[s]] = (int32_t)(base + j);
+  for (int s = 0; s < 4; ++s) {
+    const int j = wave * 256 + s * 64 + lane;
+    if (j < len) {
+      int pre = 0;
+      for (int ww = 0; ww < wave; ++ww) pre += wcnt[ww][lbl[s]];
+      perm[(long long)bh * N + off[lbl[s]] + pre + rank[s]] = (int32_t)(base + j);
+    }
   }
 }
 
