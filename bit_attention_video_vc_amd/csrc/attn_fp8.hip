@@ -278,17 +278,31 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
           for (int r = 0; r < 16; ++r) s[m][r] = fminf(s[m][r], (56.0f - Bc) / A);
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < 4; ++m) {
+        uint32_t wv[4];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           uint32_t w = 0u;
 #pragma unroll
           for (int b = 0; b < 4; ++b)   // round to nearest even, clamp to [0,255], pack
             w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[m][4 * r4 + b], A, Bc), b, w);
-          // flush codes 1..7 (below the E4M3 normal range) to 0, four bytes at a time
-          const uint32_t keep = (w + 0x78787878u) & 0x80808080u;
-          pk[4 * m + r4] = w & (keep - (keep >> 7));
+          wv[r4] = w;
         }
+        // flush codes 1..7 (below the E4M3 normal range) to 0, eight bytes at a
+        // time: codes are <= 56, so adding 0x78 to every byte carries nowhere and
+        // sets a byte's top bit exactly when its code is >= 8; V_PERM_B32 spreads
+        // those top bits (bytes 1, 3 directly, bytes 0, 2 from the copy shifted
+        // left by 8) into byte masks.
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const uint64_t w64 = ((uint64_t)wv[2 * pr + 1] << 32) | wv[2 * pr];
+          const uint64_t t = w64 + 0x7878787878787878ull;
+          const uint64_t t8 = t << 8;
+          pk[4 * m + 2 * pr] = wv[2 * pr] & __builtin_amdgcn_perm((uint32_t)t8, (uint32_t)t, 0x090B080Au);
+          pk[4 * m + 2 * pr + 1] =
+              wv[2 * pr + 1] & __builtin_amdgcn_perm((uint32_t)(t8 >> 32), (uint32_t)(t >> 32), 0x090B080Au);
+        }
+      }
     } else {   // VC_P_FP32EXP_E4M3: conventional exp2 then E4M3 conversion
 #pragma unroll
       for (int m = 0; m < 4; ++m)
