@@ -68,9 +68,9 @@ enum vc_v_format {
 
 /* ------------------------------------------------------------------------
  * V-Smooth grouping: k-means over Value tokens per (batch, head), then a stable
- * sort by cluster label (paper digest, V-Smooth paragraph: "each batch and head
- * runs online k-means on Value tokens and reorders Key and Value by label";
- * news article, "V-Smooth", item Group).
+ * sort by cluster label (paper digest, V-Smooth paragraph: k-means runs per batch
+ * and head over the Value tokens at inference time, and Key and Value are
+ * reordered together by label; news article, "V-Smooth", item Group).
  *
  * Arithmetic (fixed so that the result is reproducible bit for bit):
  *   init     centroid c = V[floor(c*N/k)] (as fp32)

@@ -35,7 +35,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
-BLOCK = 128          # hardware block of the method (V-Smooth: "each 128-token block")
+BLOCK = 128          # block size of the method (V-Smooth demeans 128-token blocks)
 LOG2E = 1.4426950408889634
 E4M3_MAX = 448.0
 E2M1_MAX = 6.0
@@ -175,8 +175,8 @@ def kmeans(v_f32: np.ndarray, k: int, iters: int):
     """k-means over the Value tokens of one (batch, head).
 
     [digest] V-Smooth paragraph: each batch and head runs online k-means over its
-    Value tokens.  [news] "V-Smooth", item Group.  "Online" is read as "at
-    inference time, per call" (Lloyd iterations, as the configurations state).
+    Value tokens.  [news] "V-Smooth", item Group.  Online is read as run at
+    inference time on every call (Lloyd iterations, as the configurations state).
     The fixed arithmetic (see vc_oracle.c) is the reading taken.
     Returns (labels int32 [N], centroids float32 [k, d], counts int64 [k]).
     """
