@@ -261,6 +261,14 @@ def main():
                             "speedup_of_fp8_kernel": round(ms_bf16 / ms_attn, 3)},
         "fidelity_rel_l2_vs_exact_fp32": {"attn_fp8_expcast": float(f"{fid_fp8:.4e}"),
                                           "attn_bf16": float(f"{fid_bf16:.4e}"), "rows": fid_rows},
+        # grouping cadence of the pages (first quarter of the denoising steps, each
+        # permutation reused for four steps): grouping time over the trajectory as a
+        # share of its attention calls (preprocess + attention), from the stage times
+        "grouping_amortized": {
+            "grouping_step_overhead": round(ms_group / (ms_prep + ms_attn), 4),
+            "share_of_attention_time": {str(T): round(vc.group_count(T) * ms_group / (T * (ms_prep + ms_attn)), 5)
+                                        for T in (40, 50)},
+        },
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "traffic": committed_traffic()},

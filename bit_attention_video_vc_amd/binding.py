@@ -49,6 +49,11 @@ def lib():
         for f in ("vc_vsmooth_group", "vc_preprocess_quant", "vc_attn_fp8_fwd", "vc_attn_bf16_fwd",
                   "vc_attn_fp8_fwd_dump"):
             getattr(L, f).restype = I
+        for f in ("vc_group_due", "vc_group_source"):
+            getattr(L, f).argtypes = [I, I, I, F]
+            getattr(L, f).restype = I
+        L.vc_group_count.argtypes = [I, I, F]
+        L.vc_group_count.restype = I
         L.vc_status_string.argtypes = [I]
         L.vc_status_string.restype = ctypes.c_char_p
         L.vc_version.restype = ctypes.c_char_p
@@ -200,3 +205,55 @@ def unswizzle_v_codes(v_codes: torch.Tensor, N: int) -> torch.Tensor:
     to row-major permuted order [B,H,Np,128] (host-side helper for checks)."""
     B, H, nb, d, r = v_codes.shape
     return v_codes.permute(0, 1, 2, 4, 3).reshape(B, H, nb * r, d)
+
+
+def group_due(step: int, total_steps: int, reuse: int = 4, fraction: float = 0.25) -> bool:
+    """True if denoising step `step` computes a new V-Smooth permutation (include/vc.h)."""
+    r = lib().vc_group_due(step, total_steps, reuse, fraction)
+    _check(min(r, 0), "vc_group_due")
+    return bool(r)
+
+
+def group_source(step: int, total_steps: int, reuse: int = 4, fraction: float = 0.25) -> int:
+    """The step whose permutation denoising step `step` uses."""
+    r = lib().vc_group_source(step, total_steps, reuse, fraction)
+    _check(min(r, 0), "vc_group_source")
+    return r
+
+
+def group_count(total_steps: int, reuse: int = 4, fraction: float = 0.25) -> int:
+    """Number of regrouping steps over a trajectory of `total_steps`."""
+    r = lib().vc_group_count(total_steps, reuse, fraction)
+    _check(min(r, 0), "vc_group_count")
+    return r
+
+
+class PermutationCache:
+    """One V-Smooth permutation per attention layer across a denoising trajectory.
+
+    `perm(layer, step, V)` regroups when the cadence says so (vc_group_due) and
+    otherwise returns the permutation cached for that layer, after checking that
+    it came from the step the cadence names (vc_group_source).  `group_fn` is
+    vsmooth_group unless given (it must return the permutation first).
+    """
+
+    def __init__(self, total_steps: int, reuse: int = 4, fraction: float = 0.25, k: int = 64, iters: int = 8,
+                 group_fn=None):
+        group_count(total_steps, reuse, fraction)   # validates the cadence
+        self.total_steps, self.reuse, self.fraction = total_steps, reuse, fraction
+        self.k, self.iters = k, iters
+        self.group_fn = group_fn if group_fn is not None else (lambda V, k, it: vsmooth_group(V, k, it))
+        self._perms = {}
+        self.group_calls = 0
+
+    def perm(self, layer, step: int, V):
+        if group_due(step, self.total_steps, self.reuse, self.fraction):
+            self._perms[layer] = (step, self.group_fn(V, self.k, self.iters)[0])
+            self.group_calls += 1
+            return self._perms[layer][1]
+        src = group_source(step, self.total_steps, self.reuse, self.fraction)
+        cached = self._perms.get(layer)
+        if cached is None or cached[0] != src:
+            have = None if cached is None else cached[0]
+            raise VcError(f"layer {layer!r}, step {step}: needs the permutation of step {src}, cache holds {have}")
+        return cached[1]

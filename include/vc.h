@@ -186,6 +186,29 @@ int vc_attn_fp8_fwd_dump(const uint8_t* q_codes, const float* q_scales,
                          int B, int H, int N, int d, float softmax_scale, int p_mode,
                          float* out, float* s_dump, uint8_t* p_dump, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Grouping cadence over a denoising trajectory (paper digest, clustering-
+ * rationale paragraph and limitations; news article, "V-Smooth"; insight
+ * article, "Value Is the Error Source Earlier Methods Underestimated"): grouping
+ * runs only during the first quarter of the denoising steps, and each
+ * permutation serves four adjacent steps.  Host-only calls; no GPU work.
+ *
+ * Reading: step s (0-based, 0 <= s < total_steps) lies in the grouping window
+ * when s < fraction * total_steps (as real numbers); a step in the window
+ * regroups when s % reuse == 0, so step 0 always regroups.  Every step uses the
+ * permutation of the latest regrouping step at or before it; steps past the
+ * window keep the last one.  The pages' cadence is reuse = 4, fraction = 0.25.
+ *
+ * vc_group_due     1 if step s computes a new permutation, 0 if it reuses one
+ * vc_group_source  the step whose permutation step s uses
+ * vc_group_count   regrouping steps over the whole trajectory
+ * Each returns VC_ERR_INVALID_ARG when total_steps < 1, step is outside
+ * [0, total_steps), reuse < 1 or fraction is outside (0, 1].
+ * ------------------------------------------------------------------------ */
+int vc_group_due(int step, int total_steps, int reuse, float fraction);
+int vc_group_source(int step, int total_steps, int reuse, float fraction);
+int vc_group_count(int total_steps, int reuse, float fraction);
+
 const char* vc_status_string(int status);
 int vc_last_hip_error(void);
 const char* vc_version(void);
