@@ -283,7 +283,66 @@ def _block_scaled_e4m3(x: np.ndarray, N: int):
     return codes, scales
 
 
-def preprocess_head(q_bf16, k_bf16, v_bf16, perm, v_format: str = "e4m3"):
+def rope_f32(x: np.ndarray, cs: np.ndarray) -> np.ndarray:
+    """Rotary position embedding of Q or K rows, as a step of the fused
+    preprocessing.
+
+    [digest] preprocessing paragraph: RoPE is one of the steps fused into the
+    quantisation kernel.  The pages do not define the rotation; the reading is
+    the usual pairwise one, with the angles supplied by the caller: `cs` is a
+    float32 table [rows, 64, 2] of (cos, sin) for each row and channel pair
+    (2i, 2i+1), and in float32
+        y_2i   = fmaf(x_2i, c, -(x_2i+1 * s))
+        y_2i+1 = fmaf(x_2i, s,   x_2i+1 * c)
+    with each inner product rounded once.  x: float32 [rows, 128].
+    """
+    x = f32(x)
+    cs = f32(cs)
+    x0, x1 = x[:, 0::2], x[:, 1::2]
+    c, s = cs[..., 0], cs[..., 1]
+    out = np.empty_like(x)
+    out[:, 0::2] = fma_f32(x0, c, -f32(x1 * s))
+    out[:, 1::2] = fma_f32(x0, s, f32(x1 * c))
+    return out
+
+
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform along the last axis, y = H x with
+    H[i][j] = (-1)^popcount(i & j) (Sylvester order), in float32 stage by stage:
+    for h = 1, 2, 4, ..., d/2 the pair (i, i + h) with i & h == 0 becomes
+    (a + b, a - b), each rounded once.
+
+    [digest] preprocessing paragraph (Hadamard is one of the fused steps) and
+    results paragraph (a Hadamard on Q and K moves PSNR by 0.1-0.3 dB at most).
+    """
+    y = f32(x).copy()
+    d = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < d:
+        z = y.reshape(*lead, d // (2 * h), 2, h)
+        a, b = z[..., 0, :], z[..., 1, :]
+        y = np.stack([f32(a + b), f32(a - b)], axis=-2).reshape(*lead, d)
+        h *= 2
+    return y
+
+
+def qk_transform(x: np.ndarray, cs=None, hadamard: bool = False, k_side: bool = False) -> np.ndarray:
+    """RoPE (when a table is given) then the Hadamard (when asked) of Q or K rows
+    in float32, before the per-block E4M3 quantisation.  Reading for the
+    Hadamard: Q' = H q and K' = 2^-7 H k (an exact power-of-two scale), so that
+    Q'.K' = q.k exactly in real arithmetic (H H^T = 128 I)."""
+    y = f32(x)
+    if cs is not None:
+        y = rope_f32(y, cs)
+    if hadamard:
+        y = fwht_f32(y)
+        if k_side:
+            y = f32(y * F32(2.0 ** -7))
+    return y
+
+
+def preprocess_head(q_bf16, k_bf16, v_bf16, perm, v_format: str = "e4m3", rope_cs=None, hadamard: bool = False):
     """Gather, demean and quantise one (batch, head).
 
     [digest] V-Smooth paragraph (reorder K and V by label; subtract each 128-row
@@ -294,10 +353,17 @@ def preprocess_head(q_bf16, k_bf16, v_bf16, perm, v_format: str = "e4m3"):
     Readings: "per-channel" = one scale per (batch, head, channel) over all N
     tokens, sv = amax/448; residual R = fp32(v) - fp32(mean) in float32;
     codes = E4M3(R * (448/amax)) in float32.  Q stays in the original order.
+    With `rope_cs` ([N, 64, 2], original token order) and/or `hadamard`, Q and
+    K rows go through qk_transform first (K rows keep their original position).
     """
     N = v_bf16.shape[0]
     qf = bf16_to_f32(q_bf16) if q_bf16 is not None else None
-    kp = bf16_to_f32(k_bf16)[perm]
+    if rope_cs is not None or hadamard:
+        if qf is not None:
+            qf = qk_transform(qf, rope_cs, hadamard, k_side=False)
+        kp = qk_transform(bf16_to_f32(k_bf16), rope_cs, hadamard, k_side=True)[perm]
+    else:
+        kp = bf16_to_f32(k_bf16)[perm]
     vp = bf16_to_f32(v_bf16)[perm]
     nb = n_blocks(N)
     means = block_means(vp)
@@ -520,10 +586,12 @@ def exact_attention(q_bf16, k_bf16, v_bf16, softmax_scale: float, rows=None) -> 
 # Whole-tensor drivers and diagnostics
 # ---------------------------------------------------------------------------
 
-def preprocess(Q, K, V, perm, v_format="e4m3"):
-    """[B, H, N, d] bf16 bits (Q may be None) -> list of per-head dicts."""
+def preprocess(Q, K, V, perm, v_format="e4m3", rope_cs=None, hadamard=False):
+    """[B, H, N, d] bf16 bits (Q may be None) -> list of per-head dicts.  One
+    RoPE table [N, 64, 2] serves every (batch, head)."""
     B, H = K.shape[:2]
-    return [[preprocess_head(None if Q is None else Q[b, h], K[b, h], V[b, h], perm[b, h], v_format)
+    return [[preprocess_head(None if Q is None else Q[b, h], K[b, h], V[b, h], perm[b, h], v_format,
+                             rope_cs, hadamard)
              for h in range(H)] for b in range(B)]
 
 

@@ -72,3 +72,37 @@ def test_missing_running_max_rescale_fails_the_softmax_pin(monkeypatch):
     monkeypatch.setattr(O, "online_attention", no_rescale)
     with pytest.raises(AssertionError):
         TA.test_online_softmax_with_mean_restore_is_exact_softmax(300)
+
+
+def test_swapped_butterfly_fails_the_sylvester_pin(monkeypatch):
+    from tests import test_oracle_qk_transform as TQ
+
+    def fwht_swapped(x):
+        y = O.f32(x).copy()
+        d = y.shape[-1]
+        lead = y.shape[:-1]
+        h = 1
+        while h < d:
+            z = y.reshape(*lead, d // (2 * h), 2, h)
+            a, b = z[..., 0, :], z[..., 1, :]
+            y = np.stack([O.f32(a + b), O.f32(b - a)], axis=-2).reshape(*lead, d)   # wrong sign
+            h *= 2
+        return y
+
+    monkeypatch.setattr(O, "fwht_f32", fwht_swapped)
+    with pytest.raises(AssertionError):
+        TQ.test_fwht_matches_the_sylvester_matrix_exactly_on_integers()
+
+
+def test_wrong_rotation_sense_fails_the_quarter_turn_pin(monkeypatch):
+    from tests import test_oracle_qk_transform as TQ
+    real = O.rope_f32
+
+    def rope_inverse(x, cs):
+        cs = np.array(cs, np.float32, copy=True)
+        cs[..., 1] = -cs[..., 1]          # rotates the other way
+        return real(x, cs)
+
+    monkeypatch.setattr(O, "rope_f32", rope_inverse)
+    with pytest.raises(AssertionError):
+        TQ.test_rope_identity_and_quarter_turn()
