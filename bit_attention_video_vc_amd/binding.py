@@ -41,12 +41,13 @@ def lib():
         L.vc_preprocess_workspace.argtypes = [I, I, I, I, I]
         L.vc_preprocess_workspace.restype = Z
         L.vc_preprocess_quant.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]
+        L.vc_preprocess_quant_ex.argtypes = [P, P, P, P, I, I, I, I, I, P, I, P, P, P, P, P, P, P, P, P, Z, P]
         L.vc_attn_fp8_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, P]
         L.vc_attn_bf16_workspace.argtypes = [I, I, I, I]
         L.vc_attn_bf16_workspace.restype = Z
         L.vc_attn_bf16_fwd.argtypes = [P, P, P, I, I, I, I, F, P, P, Z, P]
         L.vc_attn_fp8_fwd_dump.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P]
-        for f in ("vc_vsmooth_group", "vc_preprocess_quant", "vc_attn_fp8_fwd", "vc_attn_bf16_fwd",
+        for f in ("vc_vsmooth_group", "vc_preprocess_quant", "vc_preprocess_quant_ex", "vc_attn_fp8_fwd", "vc_attn_bf16_fwd",
                   "vc_attn_fp8_fwd_dump"):
             getattr(L, f).restype = I
         for f in ("vc_group_due", "vc_group_source"):
@@ -107,9 +108,11 @@ def vsmooth_group(V: torch.Tensor, k: int, iters: int, want_labels=False, want_c
     return perm, labels, cents
 
 
-def preprocess_quant(Q, K, V, perm, v_format="e4m3"):
+def preprocess_quant(Q, K, V, perm, v_format="e4m3", rope_cs=None, hadamard=False):
     """Gather, block means and quantisation.  Q may be None.  Returns a dict of
-    device tensors in the layouts of include/vc.h."""
+    device tensors in the layouts of include/vc.h.  rope_cs (fp32 [N, 64, 2]
+    cos/sin table on the GPU) and hadamard select the Q/K transforms of
+    vc_preprocess_quant_ex."""
     fmt = _VFMTS[v_format] if isinstance(v_format, str) else v_format
     dev = _dev(_bits(K))
     _dev(_bits(V))
@@ -138,11 +141,16 @@ def preprocess_quant(Q, K, V, perm, v_format="e4m3"):
     L = lib()
     ws_bytes = L.vc_preprocess_workspace(B, H, N, d, fmt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    _check(L.vc_preprocess_quant(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), B, H, N, d, fmt,
-                                 _ptr(out["q_codes"]), _ptr(out["q_scales"]), _ptr(out["k_codes"]),
-                                 _ptr(out["k_scales"]), _ptr(out["v_codes"]), _ptr(out["v_scales"]),
-                                 _ptr(out["v_group_scales"]), _ptr(out["v_means"]), _ptr(ws), ws_bytes,
-                                 _stream(dev)), "vc_preprocess_quant")
+    if rope_cs is not None:
+        _dev(rope_cs)
+        if rope_cs.dtype != torch.float32 or tuple(rope_cs.shape) != (N, 64, 2):
+            raise VcError("rope_cs must be float32 [N, 64, 2]")
+    _check(L.vc_preprocess_quant_ex(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), B, H, N, d, fmt, _ptr(rope_cs),
+                                    1 if hadamard else 0,
+                                    _ptr(out["q_codes"]), _ptr(out["q_scales"]), _ptr(out["k_codes"]),
+                                    _ptr(out["k_scales"]), _ptr(out["v_codes"]), _ptr(out["v_scales"]),
+                                    _ptr(out["v_group_scales"]), _ptr(out["v_means"]), _ptr(ws), ws_bytes,
+                                    _stream(dev)), "vc_preprocess_quant_ex")
     return out
 
 

@@ -15,7 +15,9 @@
 //          amax per channel -> atomic max (E4M3) or per head (NVFP4)
 //   pass 2 (one workgroup per block): gather K and V again, K per-block E4M3,
 //          V residual codes (E4M3 with the per-channel scale, or NVFP4), Q
-//          per-block E4M3 in original order.  V codes are written transposed
+//          per-block E4M3 in original order.  Q and K rows stay in registers,
+//          optionally through RoPE and the Hadamard transform first (the same
+//          paragraph lists both among the fused steps).  V codes are written transposed
 //          per block (channel-major), the operand order of the attention kernel.
 // A small clear kernel zeroes the amax accumulators first (no memset on the
 // stream, so the sequence can be captured in a graph).
@@ -73,34 +75,83 @@ __global__ void __launch_bounds__(kD) pre_pass1(const uint16_t* __restrict__ V, 
   }
 }
 
-// Per-block E4M3 of a staged bf16 tile (Q or K): scale = amax/448.
-__device__ void encode_block_scaled(const uint16_t* tile, int n, uint8_t* __restrict__ out_rows,
-                                    float* __restrict__ scale_out, float* red) {
-  const int tid = threadIdx.x;
+// Q or K rows (optionally) through RoPE and the Walsh-Hadamard transform, then
+// per-block E4M3 with scale = amax/448, all in registers: thread 2r + p holds channels 64p .. 64p + 63 of row r
+// (256 threads, 128 rows).  Arithmetic in fp32, in the order of the method's
+// reading: RoPE on channel pairs (2i, 2i+1) with the caller's (cos, sin) of the
+// row's original position, y0 = fmaf(x0, c, -(x1 s)), y1 = fmaf(x0, s, x1 c);
+// the unnormalised Sylvester transform stage by stage (h = 1 .. 32 inside a
+// thread, h = 64 across the thread pair), (a + b, a - b); K rows then scaled by
+// 2^-7 so that Q' . K' = Q . K.  Block scale amax/448, codes E4M3(y * 448/amax).
+__device__ __forceinline__ void transform_encode(const uint16_t* __restrict__ src, const int32_t* rows, int n,
+                                 const float2* __restrict__ rope, bool hadamard, bool k_side,
+                                 uint8_t* __restrict__ out_rows, float* __restrict__ scale_out, float* red) {
+  const int tid = threadIdx.x, r = tid >> 1, p = tid & 1;
+  const bool valid = r < n;
+  float y[64];
+  if (valid) {
+    const uint16_t* rp = src + (long long)rows[r] * kD + 64 * p;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 u = *reinterpret_cast<const uint4*>(rp + 8 * j);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[8 * j + 2 * e] = __uint_as_float(w[e] << 16);
+        y[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) y[i] = 0.0f;
+  }
+  if (rope && valid) {
+    const float2* cs = rope + (long long)rows[r] * 64 + 32 * p;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float2 c = cs[i];
+      const float x0 = y[2 * i], x1 = y[2 * i + 1];
+      y[2 * i] = __builtin_fmaf(x0, c.x, -(x1 * c.y));
+      y[2 * i + 1] = __builtin_fmaf(x0, c.y, x1 * c.x);
+    }
+  }
+  if (hadamard) {
+#pragma unroll
+    for (int h = 1; h < 64; h *= 2)
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+        if ((i & h) == 0) {
+          const float a = y[i], b = y[i + h];
+          y[i] = a + b;
+          y[i + h] = a - b;
+        }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {   // h = 64: channel i (thread p = 0) with channel i + 64 (p = 1)
+      const float o = __shfl_xor(y[i], 1);
+      y[i] = p == 0 ? y[i] + o : o - y[i];
+      if (k_side) y[i] *= 0x1p-7f;
+    }
+  }
   float am = 0.0f;
-  for (int q = tid; q < n * kD; q += 256) am = fmaxf(am, fabsf(bf16_bits_to_f32(tile[q])));
+  if (valid)
+#pragma unroll
+    for (int i = 0; i < 64; ++i) am = fmaxf(am, fabsf(y[i]));
   for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
   if ((tid & 63) == 0) red[tid >> 6] = am;
   __syncthreads();
   am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float inv = am > 0.0f ? 448.0f / am : 0.0f;
   if (tid == 0) *scale_out = am > 0.0f ? am / 448.0f : 0.0f;
-  // 128 rows x 8 chunks of 16 codes
-  for (int q = tid; q < kBlock * 8; q += 256) {
-    const int r = q >> 3, c0 = (q & 7) * 16;
-    uint32_t w[4] = {0, 0, 0, 0};
-    if (r < n) {
+  uint32_t w[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a = bf16_bits_to_f32(tile[r * kD + c0 + 4 * e + 0]) * inv;
-        const float b = bf16_bits_to_f32(tile[r * kD + c0 + 4 * e + 1]) * inv;
-        const float cc = bf16_bits_to_f32(tile[r * kD + c0 + 4 * e + 2]) * inv;
-        const float d = bf16_bits_to_f32(tile[r * kD + c0 + 4 * e + 3]) * inv;
-        w[e] = pack2_e4m3_sat<true>(cc, d, pack2_e4m3_sat<false>(a, b, 0u));
-      }
-    }
-    *reinterpret_cast<uint4*>(out_rows + (long long)r * kD + c0) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  for (int e = 0; e < 16; ++e)
+    w[e] = valid ? pack2_e4m3_sat<true>(y[4 * e + 2] * inv, y[4 * e + 3] * inv,
+                                        pack2_e4m3_sat<false>(y[4 * e] * inv, y[4 * e + 1] * inv, 0u))
+                 : 0u;
+  uint8_t* op = out_rows + (long long)r * kD + 64 * p;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<uint4*>(op + 16 * j) = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
   __syncthreads();
 }
 
@@ -123,7 +174,8 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
                                                  uint8_t* __restrict__ q_codes, float* __restrict__ q_scales,
                                                  uint8_t* __restrict__ k_codes, float* __restrict__ k_scales,
                                                  uint8_t* __restrict__ v_codes, float* __restrict__ v_scales,
-                                                 uint8_t* __restrict__ v_gscales) {
+                                                 uint8_t* __restrict__ v_gscales, const float2* __restrict__ rope,
+                                                 int hadamard) {
   __shared__ __align__(16) uint16_t tile[kBlock * kD];
   __shared__ int32_t rows[kBlock];
   __shared__ float red[4];
@@ -135,9 +187,8 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
   __syncthreads();
 
   // K: gathered, per-block scale
-  stage_rows(tile, K + (long long)bh * N * kD, rows, n, 256);
-  __syncthreads();
-  encode_block_scaled(tile, n, k_codes + rowbase * kD, k_scales + (long long)bh * nb + t, red);
+  transform_encode(K + (long long)bh * N * kD, rows, n, rope, hadamard != 0, true, k_codes + rowbase * kD,
+                   k_scales + (long long)bh * nb + t, red);
 
   // V residual
   stage_rows(tile, V + (long long)bh * N * kD, rows, n, 256);
@@ -209,9 +260,8 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
   if (Q) {
     if (tid < kBlock) rows[tid] = t * kBlock + tid;
     __syncthreads();
-    stage_rows(tile, Q + (long long)bh * N * kD, rows, n, 256);
-    __syncthreads();
-    encode_block_scaled(tile, n, q_codes + rowbase * kD, q_scales + (long long)bh * nb + t, red);
+    transform_encode(Q + (long long)bh * N * kD, rows, n, rope, hadamard != 0, false, q_codes + rowbase * kD,
+                     q_scales + (long long)bh * nb + t, red);
   }
 }
 
@@ -225,17 +275,18 @@ extern "C" size_t vc_preprocess_workspace(int B, int H, int N, int d, int v_form
   return v_format == VC_V_NVFP4 ? (size_t)BH * sizeof(float) : (size_t)BH * kD * sizeof(float);
 }
 
-extern "C" int vc_preprocess_quant(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
-                                   int B, int H, int N, int d, int v_format, uint8_t* q_codes, float* q_scales,
-                                   uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
-                                   uint8_t* v_group_scales, uint16_t* v_means, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+extern "C" int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                      int B, int H, int N, int d, int v_format, const float* rope_cs, int hadamard,
+                                      uint8_t* q_codes, float* q_scales, uint8_t* k_codes, float* k_scales,
+                                      uint8_t* v_codes, float* v_scales, uint8_t* v_group_scales, uint16_t* v_means,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   if (d != kD) return VC_ERR_UNSUPPORTED;
   if (v_format != VC_V_E4M3 && v_format != VC_V_NVFP4) return VC_ERR_UNSUPPORTED;
   if (!K || !V || !perm || !k_codes || !k_scales || !v_codes || !v_scales || !v_means) return VC_ERR_INVALID_ARG;
   if (Q && (!q_codes || !q_scales)) return VC_ERR_INVALID_ARG;
   if (v_format == VC_V_NVFP4 && !v_group_scales) return VC_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || (long long)B * H > 65535) return VC_ERR_INVALID_ARG;
+  if (hadamard != 0 && hadamard != 1) return VC_ERR_INVALID_ARG;
   const size_t need = vc_preprocess_workspace(B, H, N, d, v_format);
   if (!workspace || workspace_bytes < need) return VC_ERR_WORKSPACE;
   const long long BH = (long long)B * H;
@@ -243,18 +294,29 @@ extern "C" int vc_preprocess_quant(const uint16_t* Q, const uint16_t* K, const u
   float* amax = static_cast<float*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const long long na = (long long)(need / sizeof(float));
+  const float2* rope = reinterpret_cast<const float2*>(rope_cs);
   hipLaunchKernelGGL(clear_f32, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, st, amax, na);
   const dim3 grid(nb, (unsigned)BH);
   if (v_format == VC_V_E4M3) {
     hipLaunchKernelGGL(pre_pass1<VC_V_E4M3>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
     hipLaunchKernelGGL(pre_pass2<VC_V_E4M3>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
-                       q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales);
+                       q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales, rope, hadamard);
   } else {
     hipLaunchKernelGGL(pre_pass1<VC_V_NVFP4>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
     hipLaunchKernelGGL(pre_pass2<VC_V_NVFP4>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
-                       q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales);
+                       q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales, rope, hadamard);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return vc_set_hip_error((int)e);
   return VC_OK;
+}
+
+extern "C" int vc_preprocess_quant(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                   int B, int H, int N, int d, int v_format, uint8_t* q_codes, float* q_scales,
+                                   uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
+                                   uint8_t* v_group_scales, uint16_t* v_means, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return vc_preprocess_quant_ex(Q, K, V, perm, B, H, N, d, v_format, nullptr, 0, q_codes, q_scales, k_codes,
+                                k_scales, v_codes, v_scales, v_group_scales, v_means, workspace, workspace_bytes,
+                                stream);
 }

@@ -133,6 +133,30 @@ int vc_preprocess_quant(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                         uint8_t* v_codes, float* v_scales, uint8_t* v_group_scales,
                         uint16_t* v_means, void* workspace, size_t workspace_bytes, void* stream);
 
+/* vc_preprocess_quant with the two Q/K steps the pages also fuse into the
+ * quantisation kernel (paper digest, preprocessing paragraph: RoPE and a
+ * Hadamard transform sit in the same kernel as mean, gather and quantisation;
+ * results paragraph: a Hadamard on Q and K moves PSNR by 0.1-0.3 dB at most).
+ * The pages define neither; the arithmetic read here, in fp32, row by row:
+ *   RoPE      rope_cs: fp32 [N, 64, 2] (cos, sin) per original token position and
+ *             channel pair (2i, 2i+1), shared by every (b, h); NULL = no RoPE.
+ *             y_2i = fmaf(x_2i, c, -(x_2i+1 * s)), y_2i+1 = fmaf(x_2i, s, x_2i+1 * c)
+ *             (inner products rounded once).  A K row uses its token's own
+ *             position (before the permutation).
+ *   Hadamard  hadamard = 1: y = H y, H the unnormalised 128x128 Sylvester
+ *             matrix, computed stage by stage (h = 1, 2, ..., 64; the pair
+ *             (i, i+h) with i & h == 0 becomes (a+b, a-b)); K rows are then
+ *             multiplied by 2^-7, so Q'.K' = Q.K in real arithmetic.  0 = none.
+ * Order: RoPE, Hadamard, then the per-block E4M3 of Q and K as above.  V is not
+ * transformed.  hadamard outside {0, 1} -> VC_ERR_INVALID_ARG.  Every other
+ * argument and output as in vc_preprocess_quant, which equals this call with
+ * rope_cs = NULL and hadamard = 0. */
+int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                           int B, int H, int N, int d, int v_format, const float* rope_cs, int hadamard,
+                           uint8_t* q_codes, float* q_scales, uint8_t* k_codes, float* k_scales,
+                           uint8_t* v_codes, float* v_scales, uint8_t* v_group_scales,
+                           uint16_t* v_means, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Non-causal low-bit flash attention with block-mean restore (paper digest,
  * V-Smooth paragraph: "the block mean is added back with one outer product of

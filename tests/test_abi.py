@@ -70,6 +70,10 @@ def test_argument_errors_are_synchronous(L):
     assert L.vc_preprocess_quant(*args, 0, *outs, p, 4, null) == -3
     assert L.vc_preprocess_quant(p, p, p, p, 1, 1, 8, 96, 0, *outs, p, 1 << 20, null) == -2
     assert L.vc_preprocess_quant(p, null, p, p, 1, 1, 8, 128, 0, *outs, p, 1 << 20, null) == -1
+    # the Q/K-transform variant: hadamard must be 0 or 1; the rest as above
+    assert L.vc_preprocess_quant_ex(*args, 0, null, 2, *outs, p, 1 << 20, null) == -1
+    assert L.vc_preprocess_quant_ex(*args, 7, p, 1, *outs, p, 1 << 20, null) == -2
+    assert L.vc_preprocess_quant_ex(*args, 0, p, 1, *outs, p, 4, null) == -3
     # attention: pairing of modes, d, null out
     a = [p] * 8 + [1, 1, 8, 128, 0.1]
     assert L.vc_attn_fp8_fwd(*a, 2, 0, p, null) == -2       # bf16 P with E4M3 V: not a built pairing
