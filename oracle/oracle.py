@@ -384,6 +384,8 @@ def preprocess_head(q_bf16, k_bf16, v_bf16, perm, v_format: str = "e4m3", rope_c
         out["v_res"] = e4m3_decode(codes[:N]) * sv.astype(np.float64)[None, :]
     elif v_format == "nvfp4":
         out.update(_nvfp4_encode(R, N))
+    elif v_format == "mxfp4":
+        out.update(_mxfp4_encode(R, N))
     else:
         raise ValueError(v_format)
     return out
@@ -420,6 +422,52 @@ def _nvfp4_encode(R: np.ndarray, N: int):
     nib[N:] = 0
     res = e2m1_decode(nib[:N]) * e4m3_decode(np.repeat(sg, 16, axis=0)[:N]) * np.float64(St)
     return dict(v_nibbles=nib, v_group_scales=sg, v_scales=np.array([St], np.float32), v_res=res)
+
+
+def mxfp4_groups(Np: int) -> np.ndarray:
+    """Group index of every padded permuted row for the MXFP4 residual: within
+    each 128-row block, half h (rows 64h .. 64h+63) and g = bit 4 of the row
+    offset in that half, so group (t, h, g) holds rows 64h + 16g + [0, 16) and
+    64h + 32 + 16g + [0, 16): the 32 values one lane of the block-scaled FP4
+    matrix instruction holds against the P operand layout.  Index 4t + 2h + g."""
+    u = np.arange(Np) % BLOCK
+    h = u // 64
+    g = (u % 64 // 16) % 2
+    return (np.arange(Np) // BLOCK) * 4 + 2 * h + g
+
+
+def _mxfp4_encode(R: np.ndarray, N: int):
+    """MXFP4 residual: E2M1 values with one E8M0 (power-of-two) scale per 32.
+
+    Not a format of the pages: their 4-bit path is NVFP4 ([digest] V-Smooth
+    paragraph and preprocessing paragraph), whose per-16 scales would have to
+    be applied in the softmax; MI355X's block-scaled FP4 matrix instruction
+    applies E8M0 scales itself, so this is the 4-bit V-Smooth residual in the
+    hardware's own format.  Readings: the OCP MX rule for the shared scale,
+    X = 2^(floor(log2 amax) - 2) (2 = the largest E2M1 exponent), E8M0 code
+    clamped to [0, 254]; an all-zero group gets code 0 and zero values; values
+    E2M1_RNE_SAT(R / X) (saturating at 6).  Groups: mxfp4_groups; padding rows
+    count as zero.  V carries no per-channel scale on this path (v_scales = 1).
+    Returns v_nibbles [Np, d] (row order), v_mx_scales [nb, 2(h), 2(g), d]
+    (E8M0 codes), v_scales ones [d], v_res (decoded residual [N, d], float64)."""
+    d = R.shape[1]
+    nb = n_blocks(N)
+    Np = nb * BLOCK
+    Rp = np.zeros((Np, d), np.float32)
+    Rp[:N] = R
+    gid = mxfp4_groups(Np)
+    amax = np.zeros((4 * nb, d), np.float32)
+    np.maximum.at(amax, gid, np.abs(Rp))
+    _, ex = np.frexp(amax.astype(np.float64))          # amax = m * 2^ex, m in [0.5, 1)
+    code = np.clip(ex - 1 - 2 + 127, 0, 254).astype(np.int64)
+    code = np.where(amax > 0, code, 0)
+    X = np.ldexp(np.float64(1.0), code - 127)           # exact powers of two
+    vals = f32(Rp.astype(np.float64) / X[gid])          # power-of-two division, then float32
+    nib = e2m1_encode(vals)
+    nib[N:] = 0
+    res = e2m1_decode(nib[:N]) * X[gid][:N]
+    scales = code.reshape(nb, 2, 2, d).astype(np.uint8)
+    return dict(v_nibbles=nib, v_mx_scales=scales, v_scales=np.ones(d, np.float32), v_res=res)
 
 
 # ---------------------------------------------------------------------------

@@ -120,3 +120,72 @@ def test_fma_f32_is_one_rounding():
     got = O.fma_f32(a, b, c)
     for i in range(len(cases)):
         assert got[i] == _exact_fma_f32(a[i], b[i], c[i]), cases[i]
+
+
+# ---- MXFP4 residual (E2M1 values, E8M0 scale per 32) -------------------------
+
+def test_mxfp4_groups_are_the_lane_sets_of_32():
+    g = O.mxfp4_groups(256)
+    assert np.bincount(g).tolist() == [32] * 8
+    blk = g[:128]
+    assert set(np.nonzero(blk == 0)[0]) == set(range(0, 16)) | set(range(32, 48))
+    assert set(np.nonzero(blk == 1)[0]) == set(range(16, 32)) | set(range(48, 64))
+    assert set(np.nonzero(blk == 2)[0]) == set(range(64, 80)) | set(range(96, 112))
+    assert set(np.nonzero(blk == 3)[0]) == set(range(80, 96)) | set(range(112, 128))
+    assert np.array_equal(g[128:], g[:128] + 4)
+
+
+def _one_group(vals, d=1):
+    """A 128-row residual whose group 0 (rows 0..15, 32..47) holds vals."""
+    R = np.zeros((128, d), np.float32)
+    rows = list(range(16)) + list(range(32, 48))
+    R[rows[:len(vals)], 0] = vals
+    return R
+
+
+@pytest.mark.parametrize("amax,code", [(6.0, 127), (7.9, 127), (8.0, 128), (0.75, 124), (1.0, 125),
+                                       (2.0 ** -20, 105), (448.0, 133)])
+def test_mxfp4_scale_is_floor_log2_minus_two(amax, code):
+    out = O._mxfp4_encode(_one_group([amax, -amax / 3]), 128)
+    assert int(out["v_mx_scales"][0, 0, 0, 0]) == code
+    # the other groups of the block are empty: code 0, zero values
+    assert not out["v_mx_scales"][0, 1].any() and not out["v_mx_scales"][0, 0, 1].any()
+
+
+def test_mxfp4_saturates_and_round_trips_the_grid():
+    X = 2.0 ** -3                              # amax 0.75 -> scale 2^-3
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    vals = np.concatenate([grid * X, -grid[1:] * X, [0.75]]).astype(np.float32)
+    out = O._mxfp4_encode(_one_group(vals), 128)
+    rows = list(range(16)) + list(range(32, 48))
+    got = out["v_res"][rows[:len(vals)], 0]
+    assert np.array_equal(got, vals.astype(np.float64))
+    # 7.9 with scale 1 saturates to 6
+    sat = O._mxfp4_encode(_one_group([7.9]), 128)
+    assert sat["v_res"][0, 0] == 6.0
+
+
+def test_mxfp4_matches_brute_force_nearest_even():
+    rng = np.random.default_rng(3)
+    N = 200
+    R = (rng.standard_normal((N, 4)) * np.exp(rng.uniform(-3, 3, (1, 4)))).astype(np.float32)
+    out = O._mxfp4_encode(R, N)
+    gid = O.mxfp4_groups(256)[:N]
+    codes = out["v_mx_scales"].reshape(-1, 4)          # [4 nb, d] in index 4t + 2h + g
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    for j in range(N):
+        for c in range(4):
+            X = 2.0 ** (int(codes[gid[j], c]) - 127)
+            a = abs(float(R[j, c])) / X
+            dist = np.abs(grid - min(a, 6.0))
+            best = np.nonzero(dist == dist.min())[0]
+            k = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]   # ties to the even code
+            want = np.copysign(grid[k] * X, R[j, c]) if grid[k] > 0 else 0.0
+            assert out["v_res"][j, c] == want or (want == 0 and out["v_res"][j, c] == 0)
+    # and every group's scale code is floor(log2 amax) - 2 + 127
+    amax = np.zeros((8, 4))
+    np.maximum.at(amax, gid, np.abs(R.astype(np.float64)))
+    for q in range(8):
+        for c in range(4):
+            if amax[q, c] > 0:
+                assert int(codes[q, c]) == int(np.floor(np.log2(amax[q, c]))) - 2 + 127
