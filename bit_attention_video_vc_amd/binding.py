@@ -14,9 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(HERE, "libvc.so")
 
 P_EXPCAST, P_FP32EXP_E4M3, P_FP32_BF16 = 0, 1, 2
-V_E4M3, V_NVFP4 = 0, 1
+V_E4M3, V_NVFP4, V_MXFP4 = 0, 1, 2
 _PMODES = {"expcast": P_EXPCAST, "fp32exp_e4m3": P_FP32EXP_E4M3, "fp32_bf16": P_FP32_BF16}
-_VFMTS = {"e4m3": V_E4M3, "nvfp4": V_NVFP4}
+_VFMTS = {"e4m3": V_E4M3, "nvfp4": V_NVFP4, "mxfp4": V_MXFP4}
 D = 128
 BLOCK = 128
 
@@ -133,6 +133,10 @@ def preprocess_quant(Q, K, V, perm, v_format="e4m3", rope_cs=None, hadamard=Fals
         out["v_codes"] = torch.empty(B, H, nb, d, BLOCK, **u8)
         out["v_scales"] = torch.empty(B, H, d, **f32)
         out["v_group_scales"] = None
+    elif fmt == V_MXFP4:
+        out["v_codes"] = torch.empty(B, H, nb, d, BLOCK // 2, **u8)
+        out["v_scales"] = torch.empty(B, H, d, **f32)
+        out["v_group_scales"] = torch.empty(B, H, nb, d, 2, 2, **u8)
     else:
         out["v_codes"] = torch.empty(B, H, nb, d, BLOCK // 2, **u8)
         out["v_scales"] = torch.empty(B, H, **f32)

@@ -47,6 +47,7 @@ struct AttnArgs {
   const uint8_t* k;  const float* ks;
   const uint8_t* v;  const float* vs;
   const uint16_t* means;
+  const uint8_t* vg;   // MXFP4: E8M0 group scales [BH][nb][128][2(g)][2(h)]
   float* out;
   float* sdump; uint8_t* pdump;
   int N, nb, BH;
@@ -55,6 +56,18 @@ struct AttnArgs {
 
 __device__ __forceinline__ v16f mfma_f32x2(float a, float b, const v16f& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// P.V with an MXFP4 V^T operand: A = 32 E2M1 values per lane (16 bytes, the
+// upper half of the operand unused), B = P bytes (E4M3), the lane's E8M0 scale
+// in byte H of `scale` (V_MFMA_SCALE_F32_32X32X64_F8F6F4, A format FP4).  Lane
+// (row r, group g) holds keys 16g + [0, 16) and 32 + 16g + [0, 16) of the
+// 64-key chunk against B lanes holding keys 32g + [0, 32): the instruction's
+// operand layout, probed on the device.
+template <int H>
+__device__ __forceinline__ v16f mfma_pv_fp4(uint4 a4, const v8i& p, int scale, const v16f& c) {
+  const v8i a = {(int)a4.x, (int)a4.y, (int)a4.z, (int)a4.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p, c, 4, 0, H, scale, 0, 127);
 }
 
 __device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, const v4f& c) {
@@ -82,8 +95,12 @@ __device__ __forceinline__ void mfma_phase_end() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int kPMode, bool kDump>
+template <int kPMode, bool kDump, int kVF>
 __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
+  constexpr bool kFP4 = kVF == VC_V_MXFP4;
+  // V tile bytes in global memory: E4M3 128 x 128; MXFP4 128 channels x 64
+  // bytes, then (in LDS only) the 512 bytes of E8M0 scales at offset 8192
+  constexpr int kVTile = kFP4 ? kTile / 2 : kTile;
   // The two buffers of each operand are separate LDS objects so that reads of
   // one are not ordered behind the asynchronous copies into the other (the
   // copies are tracked by the vector memory counter).
@@ -133,7 +150,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
       float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.qs[(long long)bh * nb + qb])));
 
   const uint8_t* kbase = a.k + (long long)bh * Np * kD;
-  const uint8_t* vbase = a.v + (long long)bh * nb * kTile;
+  const uint8_t* vbase = a.v + (long long)bh * nb * kVTile;
   const uint16_t* mbase = a.means + (long long)bh * nb * kD;
 
   // K and V^T tiles go global -> LDS directly.  Instruction j (16 per tile,
@@ -148,13 +165,20 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   uint32_t mr = 0;
   float ksn = 0.0f;   // K scale of the block in flight; becomes the next block's
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)nb * kTile);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)nb * kTile);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)nb * kVTile);
+  // MXFP4 scales: 512 bytes per tile; lanes 32..63 of the copy read the next
+  // tile's (or, past the end, zeros) into unused LDS bytes
+  const __amdgpu_buffer_rsrc_t vgrs = make_rsrc(kFP4 ? a.vg + (long long)bh * nb * 512 : a.v, (uint32_t)nb * 512);
   uint32_t dkoff, dvoff;   // copy j = wave + 8i: rows of i = 0, 1 differ by 64 (neither swizzle changes)
   {
     const int pos = lane & 7;
     const int row = 8 * wave + (lane >> 3);
     dkoff = (uint32_t)(row * kD + 16 * (pos ^ swz_k(row)));
     dvoff = (uint32_t)(row * kD + 16 * (pos ^ swz_v(row)));
+    if (kFP4) {   // one copy per wavefront: channel rows 16 wave .. 16 wave + 15, 4 chunks of 16 bytes each
+      const int r4 = 16 * wave + (lane >> 2);
+      dvoff = (uint32_t)(r4 * 64 + 16 * ((lane & 3) ^ ((r4 >> 2) & 3)));
+    }
   }
   auto load_tile = [&](int t, int buf) {
     const uint32_t toff = (uint32_t)t * kTile;
@@ -162,7 +186,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     for (int i = 0; i < 2; ++i) {
       const int j = wave + 8 * i;
       dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * j, dkoff, toff + 8192u * i);
-      dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * j, dvoff, toff + 8192u * i);
+      if (!kFP4) dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * j, dvoff, toff + 8192u * i);
+    }
+    if (kFP4) {
+      dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * wave, dvoff, (uint32_t)t * kVTile);
+      if (wave == 0) dma16_buf(vgrs, (buf ? Vs1 : Vs0) + 8192, (uint32_t)lane * 16u, (uint32_t)t * 512u);
     }
     if (tid < kD) mr = mbase[(long long)t * kD + tid];
     ksn = a.ks[(long long)bh * nb + t];   // K scale of the block being copied
@@ -217,6 +245,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
       lv[i] = (uint32_t)(col * kD + 16 * (c ^ vsw));
     }
   }
+  // MXFP4 V^T operand: channel row 32cb + col, chunk 2h + g, swizzled like the copy
+  uint32_t lv4[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) lv4[h] = (uint32_t)(col * 64 + 16 * ((2 * h + g) ^ ((col >> 2) & 3)));
   auto ld16 = [](const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); };
   auto op8 = [](uint4 lo, uint4 hi) {
     v8i r;
@@ -351,8 +383,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
       for (int i = 0; i < 8; ++i) pop[i] = (int)pk[8 * h + i];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const uint8_t* vb = (buf ? Vs1 : Vs0) + kD * 32 * cb;
-        o[cb] = mfma32(op8(ld16(vb + lv[2 * h]), ld16(vb + lv[2 * h + 1])), pop, o[cb]);
+        if constexpr (kFP4) {
+          const uint8_t* vb = (buf ? Vs1 : Vs0) + 64 * 32 * cb;
+          const int sc = (int)*reinterpret_cast<const uint16_t*>((buf ? Vs1 : Vs0) + 8192 + (32 * cb + col) * 4 + 2 * g);
+          o[cb] = h == 0 ? mfma_pv_fp4<0>(ld16(vb + lv4[0]), pop, sc, o[cb])
+                         : mfma_pv_fp4<1>(ld16(vb + lv4[1]), pop, sc, o[cb]);
+        } else {
+          const uint8_t* vb = (buf ? Vs1 : Vs0) + kD * 32 * cb;
+          o[cb] = mfma32(op8(ld16(vb + lv[2 * h]), ld16(vb + lv[2 * h + 1])), pop, o[cb]);
+        }
       }
       rs = mfma16(ones, pop, rs);
     }
@@ -407,15 +446,18 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   }
 }
 
-static int launch_e4m3(const AttnArgs& a, int p_mode, bool dump, hipStream_t st) {
+static int launch_e4m3(const AttnArgs& a, int p_mode, bool dump, hipStream_t st, bool fp4 = false) {
   const dim3 grid((unsigned)(((a.nb + 1) / 2) * a.BH));   // one workgroup per pair of query blocks
   const dim3 block(kAttnThreads);
-  if (p_mode == VC_P_EXPCAST) {
-    if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, false>), grid, block, 0, st, a);
+  if (fp4) {
+    if (p_mode == VC_P_EXPCAST) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, false, VC_V_MXFP4>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, false, VC_V_MXFP4>), grid, block, 0, st, a);
+  } else if (p_mode == VC_P_EXPCAST) {
+    if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, true, VC_V_E4M3>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, false, VC_V_E4M3>), grid, block, 0, st, a);
   } else {
-    if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, false>), grid, block, 0, st, a);
+    if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, true, VC_V_E4M3>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, false, VC_V_E4M3>), grid, block, 0, st, a);
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VC_OK : vc_set_hip_error((int)e);
@@ -448,9 +490,15 @@ extern "C" int vc_attn_fp8_fwd(const uint8_t* q_codes, const float* q_scales, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float c0 = score_scale_c0(softmax_scale);
   if (v_format == VC_V_E4M3 && (p_mode == VC_P_EXPCAST || p_mode == VC_P_FP32EXP_E4M3)) {
-    AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means, out, nullptr, nullptr,
+    AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means, nullptr, out, nullptr, nullptr,
                N, nb, B * H, c0};
     return launch_e4m3(a, p_mode, false, st);
+  }
+  if (v_format == VC_V_MXFP4 && (p_mode == VC_P_EXPCAST || p_mode == VC_P_FP32EXP_E4M3)) {
+    if (!v_group_scales) return VC_ERR_INVALID_ARG;
+    AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means, v_group_scales, out, nullptr,
+               nullptr, N, nb, B * H, c0};
+    return launch_e4m3(a, p_mode, false, st, true);
   }
   if (v_format == VC_V_NVFP4 && p_mode == VC_P_FP32_BF16) {
     if (!v_group_scales) return VC_ERR_INVALID_ARG;
@@ -471,7 +519,7 @@ extern "C" int vc_attn_fp8_fwd_dump(const uint8_t* q_codes, const float* q_scale
     return VC_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
   const int nb = (N + kBlock - 1) / kBlock;
-  AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means, out, s_dump, p_dump,
+  AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means, nullptr, out, s_dump, p_dump,
              N, nb, B * H, score_scale_c0(softmax_scale)};
   return launch_e4m3(a, p_mode, true, static_cast<hipStream_t>(stream));
 }

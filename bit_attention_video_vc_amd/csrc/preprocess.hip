@@ -225,6 +225,34 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
       *reinterpret_cast<uint4*>(v_codes + (((long long)bh * nb + t) * kD + c) * kBlock + u0) =
           make_uint4(w[0], w[1], w[2], w[3]);
     }
+  } else if (kVFmt == VC_V_MXFP4) {
+    // MXFP4: E2M1 values, one E8M0 scale per group of 32 rows of a channel:
+    // group (h, g) = rows 64h + 16g + [0, 16) and 64h + 32 + 16g + [0, 16),
+    // the values one lane of the block-scaled FP4 MFMA holds.  Scale code
+    // floor(log2 amax) - 2 + 127 (the exponent field of amax minus 2, clamped
+    // at 0); values E2M1_RNE_SAT(R * 2^(127 - code)), an exact scaling.
+    if (t == 0 && tid < kD) v_scales[(long long)bh * kD + tid] = 1.0f;
+    for (int q = tid; q < kD * 4; q += 256) {
+      const int c = q >> 2, h = (q >> 1) & 1, gg = q & 1;
+      const float mu = bf16_bits_to_f32(means[((long long)bh * nb + t) * kD + c]);
+      float r[32];
+      float gam = 0.0f;
+#pragma unroll
+      for (int z = 0; z < 32; ++z) {
+        const int u = 64 * h + 16 * gg + (z < 16 ? z : 16 + z);
+        r[z] = u < n ? bf16_bits_to_f32(tile[u * kD + c]) - mu : 0.0f;
+        gam = fmaxf(gam, fabsf(r[z]));
+      }
+      const int eb = (int)((__float_as_uint(gam) >> 23) & 0xFFu);
+      const int code = eb >= 2 ? eb - 2 : 0;
+      const float xinv = __uint_as_float((uint32_t)(254 - code) << 23);
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int z = 0; z < 32; ++z) w[z >> 3] |= e2m1_rne_sat(r[z] * xinv) << (4 * (z & 7));
+      const long long cb = ((long long)bh * nb + t) * kD + c;
+      *reinterpret_cast<uint4*>(v_codes + cb * 64 + 32 * h + 16 * gg) = make_uint4(w[0], w[1], w[2], w[3]);
+      v_gscales[(cb * 2 + gg) * 2 + h] = (uint8_t)code;
+    }
   } else {
     const float St = amax[bh] / 2688.0f;             // amax_all / (6 * 448)
     const float six_st = 6.0f * St;
@@ -281,10 +309,10 @@ extern "C" int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, cons
                                       uint8_t* v_codes, float* v_scales, uint8_t* v_group_scales, uint16_t* v_means,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   if (d != kD) return VC_ERR_UNSUPPORTED;
-  if (v_format != VC_V_E4M3 && v_format != VC_V_NVFP4) return VC_ERR_UNSUPPORTED;
+  if (v_format != VC_V_E4M3 && v_format != VC_V_NVFP4 && v_format != VC_V_MXFP4) return VC_ERR_UNSUPPORTED;
   if (!K || !V || !perm || !k_codes || !k_scales || !v_codes || !v_scales || !v_means) return VC_ERR_INVALID_ARG;
   if (Q && (!q_codes || !q_scales)) return VC_ERR_INVALID_ARG;
-  if (v_format == VC_V_NVFP4 && !v_group_scales) return VC_ERR_INVALID_ARG;
+  if ((v_format == VC_V_NVFP4 || v_format == VC_V_MXFP4) && !v_group_scales) return VC_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || (long long)B * H > 65535) return VC_ERR_INVALID_ARG;
   if (hadamard != 0 && hadamard != 1) return VC_ERR_INVALID_ARG;
   const size_t need = vc_preprocess_workspace(B, H, N, d, v_format);
@@ -300,6 +328,10 @@ extern "C" int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, cons
   if (v_format == VC_V_E4M3) {
     hipLaunchKernelGGL(pre_pass1<VC_V_E4M3>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
     hipLaunchKernelGGL(pre_pass2<VC_V_E4M3>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
+                       q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales, rope, hadamard);
+  } else if (v_format == VC_V_MXFP4) {
+    hipLaunchKernelGGL(pre_pass1<VC_V_E4M3>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
+    hipLaunchKernelGGL(pre_pass2<VC_V_MXFP4>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
                        q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales, rope, hadamard);
   } else {
     hipLaunchKernelGGL(pre_pass1<VC_V_NVFP4>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);

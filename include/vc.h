@@ -63,7 +63,8 @@ enum vc_p_mode {
 /* Format of the V residual codes. */
 enum vc_v_format {
   VC_V_E4M3 = 0,  /* per-(b,h,channel) scaled E4M3 (8-bit path) */
-  VC_V_NVFP4 = 1  /* E2M1 values, E4M3 scale per 16 tokens, fp32 scale per (b,h) (4-bit path) */
+  VC_V_NVFP4 = 1, /* E2M1 values, E4M3 scale per 16 tokens, fp32 scale per (b,h) (4-bit path) */
+  VC_V_MXFP4 = 2  /* E2M1 values, E8M0 scale per 32 tokens (MI355X block-scaled FP4 MFMA; 4-bit path) */
 };
 
 /* ------------------------------------------------------------------------
@@ -110,6 +111,10 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
  *   NVFP4 V  St = amax_all/2688 per (b,h); per channel and 16 consecutive
  *            permuted rows (inside a block): sg = E4M3( g_amax / (6*St) ),
  *            nibble = E2M1_RNE_SAT( R / (dec(sg)*St) )
+ *   MXFP4 V  per channel, groups of 32 permuted rows of a block: rows 64h+16g+[0,16)
+ *            and 64h+32+16g+[0,16) (h, g in {0,1}); X = 2^(floor(log2 g_amax) - 2),
+ *            E8M0 code clamped to [0,254] (0 for an all-zero group);
+ *            nibble = E2M1_RNE_SAT( R / X ); no per-channel scale (v_scales = 1)
  *   K, Q     one scale per 128-row block: s = amax/448, code = E4M3(x*(448/amax));
  *            K blocks are in permuted order, Q blocks in original order.
  *
@@ -122,8 +127,12 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
  *            channel c sits at byte ((bh*nb + t)*128 + c)*128 + u.
  *            NVFP4: u8 [B,H,nb,128(channel),64]: byte ((bh*nb+t)*128+c)*64 + u/2
  *            holds rows u (low nibble, u even) and u+1 (high nibble).
- * v_scales   out, E4M3: fp32 [B,H,128] (sv); NVFP4: fp32 [B,H] (St)
- * v_group_scales  out, NVFP4 only: u8 [B,H,Np/16,128] E4M3 scale codes; NULL for E4M3
+ *            MXFP4: u8 [B,H,nb,128(channel),64]: the 16 bytes at 32h + 16g hold
+ *            group (h, g), nibble j (byte j/2, low nibble first) = row 64h+16g+j
+ *            for j < 16 and row 64h+32+16g+(j-16) for j >= 16.
+ * v_scales   out, E4M3: fp32 [B,H,128] (sv); NVFP4: fp32 [B,H] (St); MXFP4: fp32 [B,H,128] = 1
+ * v_group_scales  out, NVFP4: u8 [B,H,Np/16,128] E4M3 scale codes; MXFP4: u8
+ *            [B,H,nb,128(channel),2(g),2(h)] E8M0 codes; NULL for E4M3
  * v_means    out bf16 [B,H,nb,128]
  * ------------------------------------------------------------------------ */
 size_t vc_preprocess_workspace(int B, int H, int N, int d, int v_format);
