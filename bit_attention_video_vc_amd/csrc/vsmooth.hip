@@ -435,7 +435,7 @@ __global__ void __launch_bounds__(kAccThreads) kmeans_accum(const uint16_t* __re
   const int32_t* __restrict__ lab = w.labels + (long long)bh * N;
   const uint32_t* __restrict__ V32 = reinterpret_cast<const uint32_t*>(V + (long long)bh * N * kD);
   constexpr int kPerWave = kAccTok / (kAccThreads / 64);
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;
   const long long j_begin = (long long)blockIdx.x * kAccTok + (long long)wv * kPerWave;
 #pragma unroll 1
   for (int j0 = 0; j0 < kPerWave; j0 += kBatch) {
@@ -644,6 +644,9 @@ extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, i
       hipLaunchKernelGGL(kmeans_assign_mfma, gM, dim3(kAssignThreads), 0, st, V, N, k, w);
     else
       hipLaunchKernelGGL(kmeans_assign, gA, dim3(kAssignThreads), 0, st, V, N, k, w);
+    // the labels of the last assignment give the permutation; the update after
+    // it only matters when the caller asks for the centroids
+    if (it + 1 == iters && !centroids) break;
     if (lds_sums)
       hipLaunchKernelGGL(kmeans_accum<true>, gS, dim3(kAccThreads), lds, st, V, N, k, w);
     else
