@@ -168,8 +168,8 @@ int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, const uint16_t*
 
 /* ------------------------------------------------------------------------
  * Non-causal low-bit flash attention with block-mean restore (paper digest,
- * V-Smooth paragraph: "the block mean is added back with one outer product of
- * the row sums online softmax already accumulates, no second pass over V";
+ * V-Smooth paragraph: each block's mean returns as one outer product with the
+ * row sums that online softmax keeps anyway, without a second pass over V;
  * ExpCast-FP8 paragraph for VC_P_EXPCAST).
  *
  * For every query row i (original order) and KV block t (permuted order,
@@ -181,8 +181,10 @@ int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, const uint16_t*
  *   l     = 2^(mx-mx') l + sum_j dec(P)
  *   U     = 2^(mx-mx') U + sum_j dec(P) dec(v_j) + (sum_j dec(P)) mean_t
  *   O     = U / l  (per-channel V scales applied)
- * Supported pairings: (EXPCAST | FP32EXP_E4M3) with VC_V_E4M3, FP32_BF16 with
- * VC_V_NVFP4.  Inputs are the outputs of vc_preprocess_quant (same layouts).
+ * Supported pairings: (EXPCAST | FP32EXP_E4M3) with VC_V_E4M3 or VC_V_MXFP4
+ * (P.V through the block-scaled FP4 MFMA, the E8M0 group scales applied by the
+ * instruction; v_group_scales required), FP32_BF16 with VC_V_NVFP4.  Inputs are
+ * the outputs of vc_preprocess_quant (same layouts).
  * out        fp32 [B,H,N,128], original query order
  * ------------------------------------------------------------------------ */
 int vc_attn_fp8_fwd(const uint8_t* q_codes, const float* q_scales,

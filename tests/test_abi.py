@@ -67,6 +67,7 @@ def test_argument_errors_are_synchronous(L):
     outs = [p, p, p, p, p, p, null, p]
     assert L.vc_preprocess_quant(*args, 7, *outs, p, 1 << 20, null) == -2
     assert L.vc_preprocess_quant(*args, 1, *outs, p, 1 << 20, null) == -1      # NVFP4 needs group scales
+    assert L.vc_preprocess_quant(*args, 2, *outs, p, 1 << 20, null) == -1      # so does MXFP4
     assert L.vc_preprocess_quant(*args, 0, *outs, p, 4, null) == -3
     assert L.vc_preprocess_quant(p, p, p, p, 1, 1, 8, 96, 0, *outs, p, 1 << 20, null) == -2
     assert L.vc_preprocess_quant(p, null, p, p, 1, 1, 8, 128, 0, *outs, p, 1 << 20, null) == -1
@@ -78,6 +79,9 @@ def test_argument_errors_are_synchronous(L):
     a = [p] * 8 + [1, 1, 8, 128, 0.1]
     assert L.vc_attn_fp8_fwd(*a, 2, 0, p, null) == -2       # bf16 P with E4M3 V: not a built pairing
     assert L.vc_attn_fp8_fwd(*a, 0, 1, p, null) == -2       # ExpCast with NVFP4: the pages exclude it
+    assert L.vc_attn_fp8_fwd(*a, 2, 2, p, null) == -2       # bf16 P with MXFP4 V: not a built pairing
+    a6 = [p] * 6 + [null, p] + [1, 1, 8, 128, 0.1]
+    assert L.vc_attn_fp8_fwd(*a6, 0, 2, p, null) == -1      # MXFP4 needs its group scales
     assert L.vc_attn_fp8_fwd(*[p] * 8, 1, 1, 8, 64, 0.1, 0, 0, p, null) == -2
     assert L.vc_attn_fp8_fwd(*a, 0, 0, null, null) == -1
     assert L.vc_attn_bf16_fwd(p, p, p, 1, 1, 8, 64, 0.1, p, p, 1 << 20, null) == -2
