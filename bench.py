@@ -38,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
-CFG = 2
+WORKLOAD = "wan22-attention"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "attn_fp8_e4m3_wan22_traffic.md")
 ATTN_SOURCES = ("attn_fp8.hip", "attn_common.h", "vc_common.h")
 
@@ -170,12 +170,12 @@ def main():
         print("[bench] copied 1 GiB device to device", file=sys.stderr, flush=True)
         return
 
-    c = W.CONFIGS[CFG]
+    c = W.WORKLOADS[WORKLOAD]
     B, H, N = c["B"], c["H"], c["N"]
     scale = 1.0 / math.sqrt(128.0)
     dev = torch.device("cuda:0")
     t_gen = time.time()
-    Q, K, V = W.make_inputs(CFG)
+    Q, K, V = W.make_inputs(WORKLOAD)
     print(f"[bench] inputs drawn in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
     Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
     out = torch.empty(B, H, N, 128, dtype=torch.float32, device=dev)

@@ -100,11 +100,11 @@ def test_mxfp4_small(vc, N):
     _check(vc, Q, K, V, 8, 4, [(0, 0), (0, 1)])
 
 
-def test_mxfp4_config4_shape_sampled(vc):
-    """The 4-bit configuration's shape (B2 H24 N32760, last block 120 rows,
+def test_mxfp4_ragged_4bit_shape_sampled(vc):
+    """The ragged 4-bit workload's shape (B2 H24 N32760, last block 120 rows,
     k64 T8) on the MXFP4 path; two heads, 48 rows each."""
     _say("MXFP4 path at B2 H24 N32760 k64 T8, sampled heads (0,0) and (1,23)")
-    c = W.CONFIGS[4]
-    Q, K, V = W.make_inputs(4)
+    c = W.WORKLOADS["ragged-4bit"]
+    Q, K, V = W.make_inputs("ragged-4bit")
     rows = np.concatenate([np.arange(0, 32760, 701), np.arange(32750, 32760)])
     _check(vc, Q, K, V, c["k"], c["iters"], [(0, 0), (1, 23)], rows=rows)

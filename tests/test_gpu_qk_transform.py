@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 SCALE = 1.0 / math.sqrt(128.0)
 # Output vs the oracle on exact scores: the FP8 MFMA's accumulation moves a few
-# ExpCast codes by one step on Gaussian-like Q/K (as for the N(0,1) configs);
+# ExpCast codes by one step on Gaussian-like Q/K (the N(0,1) workloads);
 # the strict check replays the oracle on the kernel's own scores (1e-4).
 TOL_EXACT_S = 6e-3
 

@@ -21,18 +21,18 @@ import torch
 
 D = 128
 
-# name, shape, value recipe, V-Smooth settings, which P paths / V formats run
-CONFIGS = {
-    0: dict(name="tiny-8bit", B=1, H=2, N=1024, seed=0, recipe="gauss",
-            k=8, iters=10, v_format="e4m3", p_modes=("expcast",)),
-    1: dict(name="expcast-ablation", B=1, H=8, N=8192, seed=1, recipe="qk_outlier",
-            k=32, iters=10, v_format="e4m3", p_modes=("fp32exp_e4m3", "expcast")),
-    2: dict(name="wan2.2-14b-attention", B=1, H=40, N=75600, seed=2, recipe="clustered",
-            k=64, iters=8, v_format="e4m3", p_modes=("expcast",)),
-    3: dict(name="wan2.2-14b-vsmooth", B=1, H=40, N=75600, seed=2, recipe="clustered",
-            k=64, iters=8, v_format="e4m3", p_modes=()),
-    4: dict(name="ragged-4bit", B=2, H=24, N=32760, seed=4, recipe="clustered",
-            k=64, iters=8, v_format="nvfp4", p_modes=("fp32_bf16",)),
+# workload name -> shape, value recipe, V-Smooth settings, which P paths / V formats run
+WORKLOADS = {
+    "tiny-8bit": dict(B=1, H=2, N=1024, seed=0, recipe="gauss",
+                      k=8, iters=10, v_format="e4m3", p_modes=("expcast",)),
+    "expcast-ablation": dict(B=1, H=8, N=8192, seed=1, recipe="qk_outlier",
+                             k=32, iters=10, v_format="e4m3", p_modes=("fp32exp_e4m3", "expcast")),
+    "wan22-attention": dict(B=1, H=40, N=75600, seed=2, recipe="clustered",
+                            k=64, iters=8, v_format="e4m3", p_modes=("expcast",)),
+    "wan22-vsmooth": dict(B=1, H=40, N=75600, seed=2, recipe="clustered",
+                          k=64, iters=8, v_format="e4m3", p_modes=()),
+    "ragged-4bit": dict(B=2, H=24, N=32760, seed=4, recipe="clustered",
+                        k=64, iters=8, v_format="nvfp4", p_modes=("fp32_bf16",)),
 }
 
 
@@ -68,14 +68,14 @@ def draw_head(recipe: str, N: int, seed: int, b: int, h: int, d: int = D):
     return q, k, v
 
 
-def make_inputs(cfg_id: int, heads=None, N: int | None = None):
-    """bf16 CPU tensors Q, K, V of shape [B, H, N, d] for a configuration.
+def make_inputs(name: str, heads=None, N: int | None = None):
+    """bf16 CPU tensors Q, K, V of shape [B, H, N, d] for a named workload.
 
     heads: optional list of (b, h) to draw; the others stay zero (used to build
     sampled oracle cases without drawing the whole tensor).
     N: optional override of the sequence length (smaller parity cases).
     """
-    c = CONFIGS[cfg_id]
+    c = WORKLOADS[name]
     B, H = c["B"], c["H"]
     n = c["N"] if N is None else N
     Q = torch.zeros(B, H, n, D, dtype=torch.bfloat16)
