@@ -215,6 +215,26 @@ def test_deterministic_bitwise(vc):
     assert torch.equal(o1, o2)
 
 
+def test_permutation_alone_matches_oracle(vc):
+    """Asked for the permutation only, the grouping skips the update after the
+    last assignment; the permutation must not change (oracle, and the call that
+    also returns labels and centroids)."""
+    _say("permutation alone: B1 H3 N2000 k16 T5, with and without centroids")
+    Q, K, V = W.custom_inputs(1, 3, 2000, seed=21, recipe="clustered")
+    dev = torch.device("cuda:0")
+    Vd = V.to(dev)
+    perm_only, _, _ = vc.vsmooth_group(Vd, 16, 5)
+    perm_full, labels, _ = vc.vsmooth_group(Vd, 16, 5, want_labels=True, want_centroids=True)
+    torch.cuda.synchronize()
+    assert torch.equal(perm_only, perm_full)
+    v16 = _u16(V)
+    for h in range(3):
+        lab, _, _ = O.kmeans(O.bf16_to_f32(v16[0, h]), 16, 5)
+        np.testing.assert_array_equal(labels[0, h].cpu().numpy(), lab, err_msg=f"labels h{h}")
+        np.testing.assert_array_equal(perm_only[0, h].cpu().numpy(), O.stable_label_sort(lab, 16),
+                                      err_msg=f"perm h{h}")
+
+
 def test_bf16_comparator_matches_exact_attention(vc):
     _say("bf16 comparator: B1 H2 N1000 against exact fp64 attention")
     Q, K, V = W.custom_inputs(1, 2, 1000, seed=11, recipe="clustered")
