@@ -5,8 +5,8 @@ the Wan2.2-14B shape (B=1, H=40, N=75600 = 21x45x80 latent tokens, d=128):
   vc_vsmooth_group   k-means (k=64, 8 Lloyd iterations) + stable label sort
   vc_preprocess_quant gather, 128-row block means, E4M3 codes and scales
   vc_attn_fp8_fwd    FP8 attention with ExpCast P bytes and block-mean restore
-Inputs are seeded synthetic tensors (vc_workloads, configuration 2) already
-resident in HBM when the timed region starts.
+Inputs are seeded synthetic tensors (vc_workloads, the wan22-attention
+workload) already resident in HBM when the timed region starts.
 
 value = 4*N^2*d*H*B / step time (attention TFLOP/s of the whole step).
 roofline: the dominant kernel (the attention kernel) timed alone with HIP events
@@ -22,7 +22,7 @@ reading for a plain 1 GiB copy); null when the kernel sources differ from the
 ones the counters were taken on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --profile {attn,group,copy}   (short runs for rocprofv3)
+       python bench.py --profile {attn,group,copy,mxfp4}   (short runs for rocprofv3)
 """
 from __future__ import annotations
 
@@ -50,9 +50,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--kernel-reps", type=int, default=10)
-    ap.add_argument("--profile", choices=("attn", "group", "copy"), default=None,
+    ap.add_argument("--profile", choices=("attn", "group", "copy", "mxfp4"), default=None,
                     help="short run for a profiler: attention kernel only, grouping + preprocessing "
-                         "(Q skipped), or a plain 1 GiB device copy (counter calibration)")
+                         "(Q skipped), a plain 1 GiB device copy (counter calibration), or the MXFP4 "
+                         "(4-bit V residual) attention with both FP8 P paths")
     return ap.parse_args()
 
 
@@ -187,6 +188,14 @@ def main():
             vc.preprocess_quant(None, Kd, Vd, perm)
         torch.cuda.synchronize()
         print("[bench] grouping + preprocessing (Q skipped) x2 done", file=sys.stderr, flush=True)
+        return
+    if args.profile == "mxfp4":
+        perm, _, _ = vc.vsmooth_group(Vd, c["k"], c["iters"])
+        prep = vc.preprocess_quant(Qd, Kd, Vd, perm, "mxfp4")
+        for pm in ("expcast", "fp32exp_e4m3"):
+            ms_attn = timed(lambda: vc.attn_fp8_fwd(prep, scale, pm, out=out), args.kernel_reps, stream)
+            print(f"[bench] MXFP4 attention, {pm} x{args.kernel_reps}: {ms_attn:.3f} ms per call", file=sys.stderr,
+                  flush=True)
         return
     if args.profile == "attn":
         perm, _, _ = vc.vsmooth_group(Vd, c["k"], c["iters"])
