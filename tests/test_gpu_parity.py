@@ -267,7 +267,7 @@ def test_nvfp4_small_ragged(vc):
 
 
 def test_ragged_4bit_sampled(vc):
-    """Configuration 4 at full size (B2 H24 N32760, last block 120 rows, k64 T8,
+    """The ragged 4-bit workload at full size (B2 H24 N32760, last block 120 rows, k64 T8,
     NVFP4); two heads checked in full for grouping and codes, 48 rows each for
     the output."""
     _say("ragged 4-bit: B2 H24 N32760 k64 T8 NVFP4, sampled heads (0,0) and (1,23)")
