@@ -44,34 +44,56 @@ __global__ void clear_f32(float* p, long long n) {
   if (i < n) p[i] = 0.0f;
 }
 
-// Pass 1: block means and residual amax.  One thread per channel.
+// Pass 1: block means and residual amax.  One wavefront per 128-row block, lane
+// l on channels 2l and 2l + 1: every permuted row is one 256-byte load and all
+// 128 are in flight at once.  Each channel's sum runs over the rows in ascending
+// position, in fp32 from 0.  The residual amax max_r |v_r - mu| comes from the
+// channel's max and min: rounding is monotone and fl(a - b) = -fl(b - a), so
+// max(fl(vmax - mu), fl(mu - vmin), 0) is the same number.
 template <int kVFmt>
-__global__ void __launch_bounds__(kD) pre_pass1(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
-                                                int N, int nb, uint16_t* __restrict__ means,
-                                                float* __restrict__ amax) {
-  __shared__ __align__(16) uint16_t tile[kBlock * kD];
-  __shared__ int32_t rows[kBlock];
-  __shared__ float red[kD / 64];
-  const int t = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
+__global__ void __launch_bounds__(64) pre_pass1(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                               int N, int nb, uint16_t* __restrict__ means,
+                                               float* __restrict__ amax) {
+  const int t = blockIdx.x, bh = blockIdx.y, l = threadIdx.x;
   const int n = min(kBlock, N - t * kBlock);
-  rows[c] = c < n ? perm[(long long)bh * N + t * kBlock + c] : 0;
-  __syncthreads();
-  stage_rows(tile, V + (long long)bh * N * kD, rows, n, kD);
-  __syncthreads();
-  float acc = 0.0f;
-  for (int r = 0; r < n; ++r) acc += bf16_bits_to_f32(tile[r * kD + c]);
-  const uint32_t mb = f32_to_bf16_rne(acc / (float)n);
-  means[((long long)bh * nb + t) * kD + c] = (uint16_t)mb;
-  const float mu = bf16_bits_to_f32(mb);
-  float am = 0.0f;
-  for (int r = 0; r < n; ++r) am = fmaxf(am, fabsf(bf16_bits_to_f32(tile[r * kD + c]) - mu));
+  const int32_t* __restrict__ pr = perm + (long long)bh * N + (long long)t * kBlock;
+  const int p0 = pr[l < n ? l : 0], p1 = pr[l + 64 < n ? l + 64 : 0];
+  // the head's rows through a buffer resource: the row offset is a scalar, so a
+  // load costs one register (its result)
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(V + (long long)bh * N * kD), (short)0, (int)((uint32_t)N * kD * 2u), 0x00020000);
+  uint32_t x[kBlock];
+#pragma unroll
+  for (int r = 0; r < kBlock; ++r) {
+    const int row = __builtin_amdgcn_readlane(r < 64 ? p0 : p1, r & 63);
+    x[r] = __builtin_amdgcn_raw_buffer_load_b32(vr, 4 * l, (int)((uint32_t)row * (kD * 2u)), 0);
+  }
+  float s0 = 0.0f, s1 = 0.0f;
+  float hi0 = __uint_as_float(x[0] << 16), lo0 = hi0;
+  float hi1 = __uint_as_float(x[0] & 0xFFFF0000u), lo1 = hi1;
+  // rows past n hold row 0 again: harmless for max and min, and they add +0 to
+  // the sums (which start at +0 and so are never -0: s + 0 is s)
+#pragma unroll
+  for (int r = 0; r < kBlock; ++r) {
+    const float v0 = __uint_as_float(x[r] << 16), v1 = __uint_as_float(x[r] & 0xFFFF0000u);
+    s0 += r < n ? v0 : 0.0f;
+    s1 += r < n ? v1 : 0.0f;
+    hi0 = fmaxf(hi0, v0); lo0 = fminf(lo0, v0);
+    hi1 = fmaxf(hi1, v1); lo1 = fminf(lo1, v1);
+  }
+  const uint32_t m0 = f32_to_bf16_rne(s0 / (float)n), m1 = f32_to_bf16_rne(s1 / (float)n);
+  reinterpret_cast<uint32_t*>(means + ((long long)bh * nb + t) * kD)[l] = m0 | (m1 << 16);
+  const float mu0 = bf16_bits_to_f32(m0), mu1 = bf16_bits_to_f32(m1);
+  // + 0 and the sign clear keep a -0 out of the unsigned-ordered atomic max
+  const float a0 = __uint_as_float(__float_as_uint(fmaxf(fmaxf(hi0 - mu0, mu0 - lo0), 0.0f)) & 0x7FFFFFFFu);
+  const float a1 = __uint_as_float(__float_as_uint(fmaxf(fmaxf(hi1 - mu1, mu1 - lo1), 0.0f)) & 0x7FFFFFFFu);
   if (kVFmt == VC_V_E4M3) {
-    atomic_max_nonneg(&amax[(long long)bh * kD + c], am);
+    atomic_max_nonneg(&amax[(long long)bh * kD + 2 * l], a0);
+    atomic_max_nonneg(&amax[(long long)bh * kD + 2 * l + 1], a1);
   } else {
+    float am = fmaxf(a0, a1);
     for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
-    if ((c & 63) == 0) red[c >> 6] = am;
-    __syncthreads();
-    if (c == 0) atomic_max_nonneg(&amax[bh], fmaxf(red[0], red[1]));
+    if (l == 0) atomic_max_nonneg(&amax[bh], am);
   }
 }
 
@@ -326,15 +348,15 @@ extern "C" int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, cons
   hipLaunchKernelGGL(clear_f32, dim3((unsigned)((na + 255) / 256)), dim3(256), 0, st, amax, na);
   const dim3 grid(nb, (unsigned)BH);
   if (v_format == VC_V_E4M3) {
-    hipLaunchKernelGGL(pre_pass1<VC_V_E4M3>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
+    hipLaunchKernelGGL(pre_pass1<VC_V_E4M3>, grid, dim3(64), 0, st, V, perm, N, nb, v_means, amax);
     hipLaunchKernelGGL(pre_pass2<VC_V_E4M3>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
                        q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales, rope, hadamard);
   } else if (v_format == VC_V_MXFP4) {
-    hipLaunchKernelGGL(pre_pass1<VC_V_E4M3>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
+    hipLaunchKernelGGL(pre_pass1<VC_V_E4M3>, grid, dim3(64), 0, st, V, perm, N, nb, v_means, amax);
     hipLaunchKernelGGL(pre_pass2<VC_V_MXFP4>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
                        q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales, rope, hadamard);
   } else {
-    hipLaunchKernelGGL(pre_pass1<VC_V_NVFP4>, grid, dim3(kD), 0, st, V, perm, N, nb, v_means, amax);
+    hipLaunchKernelGGL(pre_pass1<VC_V_NVFP4>, grid, dim3(64), 0, st, V, perm, N, nb, v_means, amax);
     hipLaunchKernelGGL(pre_pass2<VC_V_NVFP4>, grid, dim3(256), 0, st, Q, K, V, perm, N, nb, amax, v_means,
                        q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales, rope, hadamard);
   }
