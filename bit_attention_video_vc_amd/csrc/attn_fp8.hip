@@ -24,9 +24,12 @@
 //    swizzle that keeps the 128-bit operand reads free of bank conflicts.
 //  * the row sum of the decoded P bytes comes from a 16x16x128 FP8 MFMA against
 //    a ones pattern (exact: every E4M3 value is a multiple of 2^-9), and the
-//    block mean is restored as U += rowsum (x) mean_t / sv with a rank-2 fp32
-//    MFMA per two KV blocks, so no VALU instruction touches the accumulators
-//    except the (rare) rescale when a running max moves.
+//    block means are restored four blocks at a time, U += sum_t rowsum_t (x)
+//    mean_t / sv, by one bf16 MFMA per 32 channels with each factor split into
+//    a bf16 pair (relative error below 2^-16), so no VALU instruction touches
+//    the accumulators except the (rare) rescale when a running max moves.  A
+//    tile's row sum is consumed at the start of the next tile, so no wavefront
+//    waits for its P.V MFMAs before the tile's barrier.
 //  * tiles are copied global -> LDS through buffer resources; the Q block scale
 //    is scalar and the next K block scale is prefetched with its copy, so no
 //    wait for a copy sits inside a tile; the row max crosses the two 32-lane
@@ -53,10 +56,6 @@ struct AttnArgs {
   int N, nb, BH;
   float c0;
 };
-
-__device__ __forceinline__ v16f mfma_f32x2(float a, float b, const v16f& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
 
 // P.V with an MXFP4 V^T operand: A = 32 E2M1 values per lane (16 bytes, the
 // upper half of the operand unused), B = P bytes (E4M3), the lane's E8M0 scale
@@ -108,7 +107,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   __shared__ __align__(16) uint8_t Ks1[kTile];
   __shared__ __align__(16) uint8_t Vs0[kTile];
   __shared__ __align__(16) uint8_t Vs1[kTile];
-  __shared__ __align__(16) float MuT[2][kD];   // mean_t / sv, stored [col][cb]: channel 32*cb + col
+  // A operands of the batched mean restore: per batch of four KV blocks, 16
+  // bytes per (channel block cb, lane half g, column col): bf16 [hi, lo, hi, 0]
+  // of mean_t / sv for channel 32 cb + col and blocks 2g, 2g + 1 of the batch.
+  __shared__ __align__(16) uint32_t MuB[2][1024];
   __shared__ float InvSv[kD];
   __shared__ float Sv[kD];
 
@@ -195,12 +197,26 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     if (tid < kD) mr = mbase[(long long)t * kD + tid];
     ksn = a.ks[(long long)bh * nb + t];   // K scale of the block being copied
   };
-  auto store_means = [&](int buf) {
-    if (tid < kD) MuT[buf][(tid & 31) * 4 + (tid >> 5)] = bf16_bits_to_f32(mr) * InvSv[tid];
+  // mean_t / sv of tile t as a bf16 pair: hi = the value truncated to bf16
+  // (exact difference), lo = the remainder rounded to bf16
+  auto store_means = [&](int t) {
+    if (tid < kD) {
+      const float mu = bf16_bits_to_f32(mr) * InvSv[tid];
+      const uint32_t hi = __float_as_uint(mu) & 0xFFFF0000u;
+      const uint32_t lo = f32_to_bf16_rne(mu - __uint_as_float(hi));
+      const int sl = t & 3;
+      uint2 w;
+      w.x = (hi >> 16) | (lo << 16);
+      w.y = hi >> 16;
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(MuB[(t >> 2) & 1]) +
+                                (((tid >> 5) * 2 + (sl >> 1)) * 32 + (tid & 31)) * 16 + 8 * (sl & 1)) = w;
+    }
   };
 
   load_tile(0, 0);
   float ksc = ksn;
+  // slots of blocks past the last one stay zero (0 x 0 in the final batch)
+  reinterpret_cast<uint4*>(&MuB[0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();          // InvSv ready
   store_means(0);
   wait_dma();
@@ -226,11 +242,34 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) ones[i] = on ? 0x38383838 : 0;
   }
-  // mean restore is batched over two KV blocks: lanes of group g hold block
-  // (2m + g)'s row sum (B operand of a rank-2 fp32 MFMA) and its mean/sv values
-  // for their channel in each 32-channel block (A operand).
-  float abat = 0.0f;
-  float mbat[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // The mean restore is batched over four KV blocks: rsb[s] holds the row sum
+  // of block s of the batch (rescaled with the accumulators while pending), and
+  // one bf16 V_MFMA_F32_32X32X16_BF16 per 32-channel block adds
+  // sum_s rsb[s] * mean_s / sv with each factor split into a bf16 pair
+  // (hi*hi + lo*hi + hi*lo, three of the 16 k-slots per block; the dropped
+  // lo*lo term and the rounding of lo are below 2^-16 of the product).
+  float rsb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // The row sum of tile t is taken into l and rsb at the start of tile t + 1
+  // (before that tile's rescale, so the arithmetic is unchanged): nothing waits
+  // for the P.V MFMAs at the end of a tile, and they drain during the barrier.
+  float rsp = 0.0f;
+  // U += sum_s rsb[s] (x) mean_s / sv for the batch held in MuB[mbuf]: lanes of
+  // half g carry blocks 2g, 2g + 1 as B k-slots [hi, hi, lo, 0] of each row sum
+  auto restore = [&](int mbuf) {
+    const float x0 = g ? rsb[2] : rsb[0];
+    const float x1 = g ? rsb[3] : rsb[1];
+    const uint32_t h0 = __float_as_uint(x0) & 0xFFFF0000u, h1 = __float_as_uint(x1) & 0xFFFF0000u;
+    const uint4 bw = make_uint4(h0 | (h0 >> 16), f32_to_bf16_rne(x0 - __uint_as_float(h0)), h1 | (h1 >> 16),
+                                f32_to_bf16_rne(x1 - __uint_as_float(h1)));
+    const v8bf bop = __builtin_bit_cast(v8bf, bw);
+    const uint8_t* mb = reinterpret_cast<const uint8_t*>(MuB[mbuf]) + (g * 32 + col) * 16;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(mb + 1024 * cb)), bop, o[cb], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rsb[i] = 0.0f;
+  };
   // LDS operand addresses: the K rows sigma(m, col) of the four 32-key blocks
   // differ by multiples of 16 rows and the V rows 32*cb + col by multiples of 32,
   // neither of which changes the swizzle, so four base offsets per operand plus
@@ -259,12 +298,19 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
 
   // one KV block; the LDS buffer index is a compile-time constant so every
   // LDS address is a base register plus an immediate offset
-  auto step = [&](const int t, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
+  auto step = [&](const int t, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;   // t % 4: block within the restore batch
+    constexpr int buf = slot & 1;
     if (t + 1 < nb) load_tile(t + 1, buf ^ 1);
 
+    // ---- row sum of the previous tile; restore of the batch it completed ----
+    if (slot != 0 || t > 0) {
+      l += rsp;
+      rsb[(slot + 3) & 3] = rsp;
+    }
     // ---- S^T = K_t . Q^T : 4 blocks of 32 keys x 32 queries ----
     mfma_phase_begin();
+    if (slot == 0 && t > 0) restore(((t >> 2) - 1) & 1);
     v16f s[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -368,9 +414,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
+#pragma unroll
+      for (int i = 0; i < slot; ++i) rsb[i] *= alpha;
     }
     l *= alpha;
-    abat *= alpha;
     mx = mx_new;
 
     // ---- O^T += V^T_t . P^T ; row sums from an all-ones operand ----
@@ -395,37 +442,29 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
       }
       rs = mfma16(ones, pop, rs);
     }
-    const float rsum = rs[0];
-    l += rsum;
-    // ---- mean restore: U += rowsum (x) mean_t / sv, two blocks per rank-2 MFMA ----
-    {
-      const float4 mu = *reinterpret_cast<const float4*>(&MuT[buf][col * 4]);
-      const bool mine = g == buf;
-      abat = mine ? rsum : abat;
-      mbat[0] = mine ? mu.x : mbat[0];
-      mbat[1] = mine ? mu.y : mbat[1];
-      mbat[2] = mine ? mu.z : mbat[2];
-      mbat[3] = mine ? mu.w : mbat[3];
-      if (buf == 1 || t + 1 == nb) {
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) o[cb] = mfma_f32x2(mbat[cb], abat, o[cb]);
-        abat = 0.0f;
-      }
-    }
+    rsp = rs[0];   // taken into l and rsb at the start of the next tile
     mfma_phase_end();
 
-    if (t + 1 < nb) store_means(buf ^ 1);
+    if (t + 1 < nb) store_means(t + 1);
     wait_dma();
     __syncthreads();
     ksc = ksn;
   };
 
-  int t = 0;
-  for (; t + 1 < nb; t += 2) {
+  for (int t = 0; t < nb; t += 4) {
     step(t, std::integral_constant<int, 0>{});
-    step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < nb) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < nb) step(t + 2, std::integral_constant<int, 2>{});
+    if (t + 3 < nb) step(t + 3, std::integral_constant<int, 3>{});
   }
-  if (t < nb) step(t, std::integral_constant<int, 0>{});
+  // the last tile's row sum and the restore of the final (possibly partial) batch
+  l += rsp;
+  {
+    const int sl = (nb - 1) & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rsb[i] = i == sl ? rsp : rsb[i];
+  }
+  restore(((nb - 1) >> 2) & 1);
 
   // ---- epilogue: O = sv * U / l, original query order ----
   if (qvalid && qrow < N) {

@@ -176,8 +176,11 @@ def test_expcast_ablation_recipe_given_scores(vc):
     _check_given_scores(vc, prep, preps, "fp32exp_e4m3")
 
 
+# block counts 1..8 cover every fill of the attention kernel's four-block
+# mean-restore batches (nb = 5: one full batch and one block; nb = 6, 8 ...)
 @pytest.mark.parametrize("B,H,N,k,iters", [(1, 3, 1000, 8, 4), (2, 1, 129, 3, 2), (1, 1, 1, 1, 1),
-                                           (1, 2, 127, 5, 3), (1, 1, 300, 256, 2), (1, 1, 700, 100, 3)])
+                                           (1, 2, 127, 5, 3), (1, 1, 300, 256, 2), (1, 1, 700, 100, 3),
+                                           (1, 2, 600, 16, 3), (1, 1, 850, 12, 2)])
 def test_ragged_and_degenerate_shapes(vc, B, H, N, k, iters):
     _say(f"ragged: B{B} H{H} N{N} k{k} T{iters}")
     Q, K, V = W.custom_inputs(B, H, N, seed=N + k, recipe="clustered")
