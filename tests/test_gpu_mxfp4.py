@@ -93,7 +93,8 @@ def _check(vc, Q, K, V, k, iters, heads, rows=None):
                 assert e2 <= TOL_GIVEN_S
 
 
-@pytest.mark.parametrize("N", [1000, 300, 128, 77])
+# N = 600: five 128-row blocks, one full four-block mean-restore batch and one more
+@pytest.mark.parametrize("N", [1000, 600, 300, 128, 77])
 def test_mxfp4_small(vc, N):
     _say(f"MXFP4 path: B1 H2 N{N} k8 T4")
     Q, K, V = W.custom_inputs(1, 2, N, seed=43, recipe="clustered")
