@@ -30,9 +30,11 @@
 //    the accumulators except the (rare) rescale when a running max moves.  A
 //    tile's row sum is consumed at the start of the next tile, so no wavefront
 //    waits for its P.V MFMAs before the tile's barrier.
-//  * tiles are copied global -> LDS through buffer resources; the Q block scale
-//    is scalar and the next K block scale is prefetched with its copy, so no
-//    wait for a copy sits inside a tile; the row max crosses the two 32-lane
+//  * tiles are copied global -> LDS through buffer resources, the next tile's
+//    copies issued between the Q.K MFMAs (not all at the start of a tile, where
+//    the eight wavefronts would queue behind each other in the address unit);
+//    the Q block scale is scalar and the next K block scale is prefetched with
+//    the copies, so no wait for a copy sits inside a tile; the row max crosses the two 32-lane
 //    halves with V_PERMLANE32_SWAP (no LDS).
 //  * workgroups are ordered head-major and handed to the 8 XCDs in contiguous
 //    ranges, so the workgroups sharing an XCD's L2 stream the same K/V blocks.
@@ -197,6 +199,23 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     if (tid < kD) mr = mbase[(long long)t * kD + tid];
     ksn = a.ks[(long long)bh * nb + t];   // K scale of the block being copied
   };
+  // copy p (0..3) of tile t: E4M3 K half 0, V half 0, K half 1, V half 1;
+  // MXFP4 K half 0, K half 1, V, E8M0 scales (wavefront 0).  Past the last tile
+  // the buffer resources read zeros into a buffer that is not read again.
+  auto copy_piece = [&](int t, int buf, int p) {
+    const uint32_t toff = (uint32_t)t * kTile;
+    if (!kFP4) {
+      const int i = p >> 1, j = wave + 8 * i;
+      if ((p & 1) == 0) dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * j, dkoff, toff + 8192u * i);
+      else dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * j, dvoff, toff + 8192u * i);
+    } else if (p < 2) {
+      dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * (wave + 8 * p), dkoff, toff + 8192u * p);
+    } else if (p == 2) {
+      dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * wave, dvoff, (uint32_t)t * kVTile);
+    } else if (wave == 0) {
+      dma16_buf(vgrs, (buf ? Vs1 : Vs0) + 8192, (uint32_t)lane * 16u, (uint32_t)t * 512u);
+    }
+  };
   // mean_t / sv of tile t as a bf16 pair: hi = the value truncated to bf16
   // (exact difference), lo = the remainder rounded to bf16
   auto store_means = [&](int t) {
@@ -301,7 +320,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   auto step = [&](const int t, auto slotc) {
     constexpr int slot = decltype(slotc)::value;   // t % 4: block within the restore batch
     constexpr int buf = slot & 1;
-    if (t + 1 < nb) load_tile(t + 1, buf ^ 1);
+    if (t + 1 < nb) {
+      if (tid < kD) mr = mbase[(long long)(t + 1) * kD + tid];
+      ksn = a.ks[(long long)bh * nb + t + 1];   // K scale of the block being copied
+    }
 
     // ---- row sum of the previous tile; restore of the batch it completed ----
     if (slot != 0 || t > 0) {
@@ -320,6 +342,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
         s[m] = mfma32(op8(ld16(kb + lk[2 * c2]), ld16(kb + lk[2 * c2 + 1])), qop[c2], s[m]);
+      // the next tile's copies, one per pair of Q.K MFMAs, so that they drain
+      // through the address unit while the MFMAs run
+      copy_piece(t + 1, buf ^ 1, m);
     }
     mfma_phase_end();
     // keys beyond N (last tile only) take no part
