@@ -181,6 +181,9 @@ int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, const uint16_t*
  *   l     = 2^(mx-mx') l + sum_j dec(P)
  *   U     = 2^(mx-mx') U + sum_j dec(P) dec(v_j) + (sum_j dec(P)) mean_t
  *   O     = U / l  (per-channel V scales applied)
+ * In the E4M3 and MXFP4 kernels the mean term is added four blocks at a time
+ * by a bf16 MFMA with each factor split into a bf16 pair (relative error of the
+ * term below 2^-16; everything else as written).
  * Supported pairings: (EXPCAST | FP32EXP_E4M3) with VC_V_E4M3 or VC_V_MXFP4
  * (P.V through the block-scaled FP4 MFMA, the E8M0 group scales applied by the
  * instruction; v_group_scales required), FP32_BF16 with VC_V_NVFP4.  Inputs are
