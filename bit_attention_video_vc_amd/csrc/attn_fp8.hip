@@ -33,9 +33,9 @@
 //  * tiles are copied global -> LDS through buffer resources, the next tile's
 //    copies issued between the Q.K MFMAs (not all at the start of a tile, where
 //    the eight wavefronts would queue behind each other in the address unit);
-//    the Q block scale is scalar and the next K block scale is prefetched with
-//    the copies, so no wait for a copy sits inside a tile; the row max crosses the two 32-lane
-//    halves with V_PERMLANE32_SWAP (no LDS).
+//    the Q block scale is scalar and the next K block scale is prefetched at
+//    the start of the tile, so no wait for a copy sits inside a tile; the row
+//    max crosses the two 32-lane halves with V_PERMLANE32_SWAP (no LDS).
 //  * workgroups are ordered head-major and handed to the 8 XCDs in contiguous
 //    ranges, so the workgroups sharing an XCD's L2 stream the same K/V blocks.
 #include <type_traits>
