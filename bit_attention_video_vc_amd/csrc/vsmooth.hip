@@ -22,6 +22,8 @@
 //                   per non-zero partial of the 2048-token block
 //   kmeans_update   new centroids, zero the accumulators, |c|^2
 //   sort_hist / sort_scan / sort_scatter   stable counting sort by label
+#include <type_traits>
+
 #include "vc_common.h"
 
 namespace vc {
@@ -427,7 +429,9 @@ template <bool kLdsSums>
 __global__ void __launch_bounds__(kAccThreads) kmeans_accum(const uint16_t* __restrict__ V, int N, int k,
                                                               KmWork w) {
   extern __shared__ __align__(16) unsigned long long psum[];   // [k][128] when kLdsSums
-  const int bh = blockIdx.y, tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+  // the wavefront index made uniform for the compiler: token indices, labels and
+  // the beyond-N test then live in scalar registers
+  const int bh = blockIdx.y, tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), ln = tid & 63;
   if (kLdsSums)
     for (int idx = tid; idx < k * kD; idx += kAccThreads) psum[idx] = 0ull;
   __syncthreads();
@@ -449,17 +453,30 @@ __global__ void __launch_bounds__(kAccThreads) kmeans_accum(const uint16_t* __re
       cl[b] = j < N ? lab[jj] : -1;   // uniform address: a scalar load
       raw[b] = V32[jj * (kD / 2) + ln];
     }
+    // rint(v * 2^24) is exact in int32 when every |v| of the batch is below 128
+    // (largest bf16 below 128: 127.5 * 2^24 < 2^31): one 32-bit conversion then,
+    // instead of the float -> int64 sequence.  Same integers either way.
+    u16x2 mb = {0, 0};
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      if (cl[b] < 0) continue;   // beyond N (uniform across the wavefront)
+    for (int b = 0; b < kBatch; ++b)
+      mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, raw[b] & 0x7FFF7FFFu));
+    const bool small = __all(mb[0] < 0x4300u && mb[1] < 0x4300u);   // |v| < 128, no inf or NaN
+    auto add_batch = [&](auto small_tag) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float xv = __uint_as_float(h ? (raw[b] & 0xFFFF0000u) : (raw[b] << 16));
-        const long long qv = (long long)__builtin_rintf(xv * 16777216.0f);
-        if (kLdsSums) atomicAdd(&psum[cl[b] * kD + 64 * h + ln], (unsigned long long)qv);
-        else atomicAdd(&gs[(long long)cl[b] * kD + 2 * ln + h], (unsigned long long)qv);
+      for (int b = 0; b < kBatch; ++b) {
+        if (cl[b] < 0) continue;   // beyond N (uniform across the wavefront)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float xv = __uint_as_float(h ? (raw[b] & 0xFFFF0000u) : (raw[b] << 16));
+          const float r = __builtin_rintf(xv * 16777216.0f);
+          const long long qv = decltype(small_tag)::value ? (long long)(int)r : (long long)r;
+          if (kLdsSums) atomicAdd(&psum[cl[b] * kD + 64 * h + ln], (unsigned long long)qv);
+          else atomicAdd(&gs[(long long)cl[b] * kD + 2 * ln + h], (unsigned long long)qv);
+        }
       }
-    }
+    };
+    if (small) add_batch(std::true_type{});
+    else add_batch(std::false_type{});
   }
   if (kLdsSums) {
     __syncthreads();
