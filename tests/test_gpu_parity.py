@@ -238,6 +238,26 @@ def test_permutation_alone_matches_oracle(vc):
                                       err_msg=f"perm h{h}")
 
 
+def test_grouping_large_values(vc):
+    """Rows with |v| >= 128 take the accumulation's int64 conversion path (the
+    others its int32 path); labels and centroids must match the oracle either way."""
+    _say("grouping, large values: B1 H2 N5000 k8 T3, tokens 1000..1299 scaled by 700")
+    g = torch.Generator().manual_seed(33)
+    V = torch.randn(1, 2, 5000, 128, generator=g)
+    V[:, :, 1000:1300] *= 700.0
+    V[:, 1, 4090:4100] = -300.0
+    V = V.to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    perm, labels, cents = vc.vsmooth_group(V.to(dev), 8, 3, want_labels=True, want_centroids=True)
+    torch.cuda.synchronize()
+    v16 = _u16(V)
+    for h in range(2):
+        lab, cen, _ = O.kmeans(O.bf16_to_f32(v16[0, h]), 8, 3)
+        np.testing.assert_array_equal(labels[0, h].cpu().numpy(), lab, err_msg=f"labels h{h}")
+        np.testing.assert_array_equal(cents[0, h].cpu().numpy(), cen, err_msg=f"centroids h{h}")
+        np.testing.assert_array_equal(perm[0, h].cpu().numpy(), O.stable_label_sort(lab, 8), err_msg=f"perm h{h}")
+
+
 def test_bf16_comparator_matches_exact_attention(vc):
     _say("bf16 comparator: B1 H2 N1000 against exact fp64 attention")
     Q, K, V = W.custom_inputs(1, 2, 1000, seed=11, recipe="clustered")
