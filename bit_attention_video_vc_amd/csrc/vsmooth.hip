@@ -328,7 +328,9 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
         bop[0][s4][q4] = (int)(wh ^ 0x80808080u);
         bop[1][s4][q4] = (int)(wl ^ 0x80808080u);
       }
-    if (grp + 1 < kMTokWG / 4 / 32 && t0 + 32 < N) load_group(t0 + 32);
+    // prefetch of the next group, unconditional (the last group reloads itself)
+    // so that the compiler keeps one copy of the row registers
+    load_group(grp + 1 < kMTokWG / 4 / 32 && t0 + 32 < N ? t0 + 32 : t0);
     // screened scores s_a = cc - 2 s_v s_c D / 254 (D = 254 D_hh + D_x) of
     // centroids 32b + 8(r/4) + 4g + r%4 (this lane's rows) with their bounds:
     // keep s_a - B, and U = min (s_a + B) over the token's centroids
