@@ -29,13 +29,20 @@ constexpr int kRowChunks = kD * 2 / 16;   // 16-byte chunks per bf16 row (16)
 
 // Stage rows of a bf16 [*, 128] tensor into LDS (row r <- src row idx[r]); rows
 // >= n are zero.  Every thread moves 16-byte chunks.
+// Staged rows keep their 16-byte chunk m at chunk m ^ ((r >> 4) & 7): the
+// transposing reads of a wavefront (eight rows 16 apart, one chunk) then fall on
+// eight different chunks and no two lanes share an LDS bank.
+__device__ __forceinline__ int tile_at(int r, int c) {
+  return r * kD + ((((c >> 3) ^ ((r >> 4) & 7)) << 3) | (c & 7));
+}
+
 __device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* __restrict__ src,
                                            const int32_t* rows, int n, int nthreads) {
   for (int q = threadIdx.x; q < kBlock * kRowChunks; q += nthreads) {
     const int r = q / kRowChunks, ch = q % kRowChunks;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (r < n) v = *reinterpret_cast<const uint4*>(src + (long long)rows[r] * kD + ch * 8);
-    *reinterpret_cast<uint4*>(lds + r * kD + ch * 8) = v;
+    *reinterpret_cast<uint4*>(lds + tile_at(r, ch * 8)) = v;
   }
 }
 
@@ -234,7 +241,7 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
 #pragma unroll
         for (int z = 0; z < 4; ++z) {
           const int u = u0 + 4 * e + z;
-          x[z] = u < n ? (bf16_bits_to_f32(tile[u * kD + c]) - mu) * inv : 0.0f;
+          x[z] = u < n ? (bf16_bits_to_f32(tile[tile_at(u, c)]) - mu) * inv : 0.0f;
         }
         w[e] = pack2_e4m3_sat<true>(x[2], x[3], pack2_e4m3_sat<false>(x[0], x[1], 0u));
         if (u0 + 4 * e >= n) w[e] = 0u;   // padding rows are zero bytes (not -0)
@@ -262,7 +269,7 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
 #pragma unroll
       for (int z = 0; z < 32; ++z) {
         const int u = 64 * h + 16 * gg + (z < 16 ? z : 16 + z);
-        r[z] = u < n ? bf16_bits_to_f32(tile[u * kD + c]) - mu : 0.0f;
+        r[z] = u < n ? bf16_bits_to_f32(tile[tile_at(u, c)]) - mu : 0.0f;
         gam = fmaxf(gam, fabsf(r[z]));
       }
       const int eb = (int)((__float_as_uint(gam) >> 23) & 0xFFu);
@@ -288,7 +295,7 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
 #pragma unroll
       for (int z = 0; z < 16; ++z) {
         const int u = u0 + z;
-        r[z] = u < n ? bf16_bits_to_f32(tile[u * kD + c]) - mu : 0.0f;
+        r[z] = u < n ? bf16_bits_to_f32(tile[tile_at(u, c)]) - mu : 0.0f;
         if (u < n) gam = fmaxf(gam, fabsf(r[z]));
       }
       const uint32_t sg = St > 0.0f ? f32_to_e4m3_sat(gam / six_st) : 0u;
