@@ -31,7 +31,7 @@ namespace vc {
 constexpr int kAssignThreads = 256;
 constexpr int kTokPerThread = 2;
 constexpr int kTokPerWG = kAssignThreads * kTokPerThread;  // 512 tokens
-constexpr int kAccThreads = 512;
+constexpr int kAccThreads = 1024;
 constexpr int kMTokWG = 2048;                              // tokens per screened-assignment workgroup
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
