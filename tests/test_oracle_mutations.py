@@ -106,3 +106,76 @@ def test_wrong_rotation_sense_fails_the_quarter_turn_pin(monkeypatch):
     monkeypatch.setattr(O, "rope_f32", rope_inverse)
     with pytest.raises(AssertionError):
         TQ.test_rope_identity_and_quarter_turn()
+
+
+# ---- the per-block Q/K quantiser and exact attention ------------------------
+
+def _quantiser(kind):
+    """_block_scaled_e4m3 with one planted mistake."""
+    def q(x, N):
+        d = x.shape[1]
+        nb = O.n_blocks(N)
+        codes = np.zeros((nb * 128, d), np.uint8)
+        scales = np.zeros(nb, np.float32)
+        fmax = np.float32(240.0 if kind == "fnuz_max" else 448.0)
+        for t in range(nb):
+            lo, hi = t * 128, min(N, (t + 1) * 128)
+            if kind == "end_aligned" and hi == N:
+                lo = max(0, N - 128)                      # last block taken as the final 128 rows
+            blk = x[lo:hi]
+            if kind == "per_row":
+                amax = np.abs(blk).max(axis=1, keepdims=True).astype(np.float32)
+            elif kind == "per_tensor":
+                amax = np.float32(np.abs(x[:N]).max())
+            else:
+                amax = np.float32(np.abs(blk).max())
+            amax = np.where(amax > 0, amax, np.float32(1)).astype(np.float32)
+            scales[t] = np.float32(np.max(amax) / fmax)
+            codes[hi - blk.shape[0]:hi] = O.e4m3_encode(O.f32(blk * O.f32(fmax / amax)))
+        return codes, scales
+    return q
+
+
+@pytest.mark.parametrize("kind,pin", [
+    ("per_row", "test_scale_is_shared_by_every_row_of_a_block"),
+    ("per_tensor", "test_blocks_are_independent"),
+    ("end_aligned", "test_partial_last_block_uses_its_own_rows_only"),
+    ("fnuz_max", "test_block_max_maps_to_448_and_scale_times_448_is_the_block_max"),
+])
+def test_planted_quantiser_mistakes_fail_a_pin(monkeypatch, kind, pin):
+    from tests import test_oracle_qk_quant as TQ
+    monkeypatch.setattr(O, "_block_scaled_e4m3", _quantiser(kind))
+    fn = getattr(TQ, pin)
+    with pytest.raises(AssertionError):
+        fn(300) if pin.startswith("test_block_max") else fn()
+
+
+def test_q_permuted_like_k_fails_the_order_pin(monkeypatch):
+    from tests import test_oracle_qk_quant as TQ
+    real = O.preprocess_head
+
+    def q_permuted(q, k, v, perm, *a, **kw):
+        return real(None if q is None else q[perm], k, v, perm, *a, **kw)
+
+    monkeypatch.setattr(O, "preprocess_head", q_permuted)
+    with pytest.raises(AssertionError):
+        TQ.test_q_blocks_in_original_order_k_blocks_in_permuted_order()
+
+
+def test_base_two_softmax_fails_the_logistic_pin(monkeypatch):
+    from tests import test_oracle_qk_quant as TQ
+    monkeypatch.setattr(O.np, "exp", np.exp2)
+    with pytest.raises(AssertionError):
+        TQ.test_exact_attention_two_keys_is_a_logistic_mix()
+
+
+def test_unscaled_scores_fail_the_brute_force_pin(monkeypatch):
+    from tests import test_oracle_qk_quant as TQ
+    real = O.exact_attention
+
+    def unscaled(q, k, v, softmax_scale, rows=None):
+        return real(q, k, v, 1.0, rows)
+
+    monkeypatch.setattr(O, "exact_attention", unscaled)
+    with pytest.raises(AssertionError):
+        TQ.test_exact_attention_matches_explicit_loops(7, 2)
