@@ -47,8 +47,10 @@ def lib():
         L.vc_attn_bf16_workspace.restype = Z
         L.vc_attn_bf16_fwd.argtypes = [P, P, P, I, I, I, I, F, P, P, Z, P]
         L.vc_attn_fp8_fwd_dump.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P]
+        L.vc_attn_fwd_dump.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, P, P, P]
+        L.vc_device_probe.argtypes = [I, P, P, I, P]
         for f in ("vc_vsmooth_group", "vc_preprocess_quant", "vc_preprocess_quant_ex", "vc_attn_fp8_fwd", "vc_attn_bf16_fwd",
-                  "vc_attn_fp8_fwd_dump"):
+                  "vc_attn_fp8_fwd_dump", "vc_attn_fwd_dump", "vc_device_probe"):
             getattr(L, f).restype = I
         for f in ("vc_group_due", "vc_group_source"):
             getattr(L, f).argtypes = [I, I, I, F]
@@ -191,6 +193,38 @@ def attn_fp8_fwd_dump(prep: dict, softmax_scale: float | None = None, p_mode="ex
                                       _ptr(prep["v_means"]), B, H, N, D, float(softmax_scale), pm,
                                       _ptr(out), _ptr(s), _ptr(p), _stream(dev)), "vc_attn_fp8_fwd_dump")
     return out, s, p
+
+
+def attn_fwd_dump(prep: dict, softmax_scale: float | None = None, p_mode="expcast"):
+    """vc_attn_fwd_dump: the attention output plus the per-(query, key) scores
+    and P values of any pairing (E4M3 bytes as uint8, bf16 P bits as int16)."""
+    pm = _PMODES[p_mode] if isinstance(p_mode, str) else p_mode
+    B, H, N = prep["B"], prep["H"], prep["N"]
+    Np = -(-N // BLOCK) * BLOCK
+    dev = prep["k_codes"].device
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    out = torch.empty(B, H, N, D, dtype=torch.float32, device=dev)
+    s = torch.empty(B, H, N, Np, dtype=torch.float32, device=dev)
+    p = torch.empty(B, H, N, Np, dtype=torch.int16 if pm == P_FP32_BF16 else torch.uint8, device=dev)
+    _check(lib().vc_attn_fwd_dump(_ptr(prep["q_codes"]), _ptr(prep["q_scales"]), _ptr(prep["k_codes"]),
+                                  _ptr(prep["k_scales"]), _ptr(prep["v_codes"]), _ptr(prep["v_scales"]),
+                                  _ptr(prep["v_group_scales"]), _ptr(prep["v_means"]), B, H, N, D,
+                                  float(softmax_scale), pm, prep["v_format"], _ptr(out), _ptr(s), _ptr(p),
+                                  _stream(dev)), "vc_attn_fwd_dump")
+    return out, s, p
+
+
+_PROBES = {"cvt_fp8": 0, "cvt_u8": 1, "exp2": 2, "mfma_32x32x64": 3, "mfma_16x16x128": 4}
+
+
+def device_probe(what: str, inp: torch.Tensor, out: torch.Tensor, n: int):
+    """vc_device_probe: run one gfx950 instruction on `inp` into `out` (device tensors)."""
+    _dev(inp)
+    _dev(out)
+    _check(lib().vc_device_probe(_PROBES[what], _ptr(inp), _ptr(out), int(n), _stream(inp.device)),
+           "vc_device_probe")
+    return out
 
 
 def attn_bf16_fwd(Q, K, V, softmax_scale: float | None = None, out=None, workspace=None):

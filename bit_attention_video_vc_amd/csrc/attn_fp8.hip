@@ -419,6 +419,20 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
         }
     }
 
+    // keys at or beyond N (last tile only): P byte 0.  Their scores were set
+    // to -inf for the row max, and -inf * kap is NaN when kap = 0 (an all-zero
+    // Q block or K block has scale 0), so the bytes are cleared after the fact.
+    if ((t + 1) * kBlock > N) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int key0 = t * kBlock + 64 * (m >> 1) + 32 * g + 16 * (m & 1) + 4 * r4;
+          const int nv = min(max(N - key0, 0), 4);   // valid keys among the four bytes
+          pk[4 * m + r4] &= nv >= 4 ? 0xFFFFFFFFu : (1u << (8 * nv)) - 1u;
+        }
+    }
+
     if (kDump && qvalid && qrow < N) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -510,18 +524,25 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   }
 }
 
-static int launch_e4m3(const AttnArgs& a, int p_mode, bool dump, hipStream_t st, bool fp4 = false) {
+template <int kPMode, bool kDump, int kVF>
+static void launch_one(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(((a.nb + 1) / 2) * a.BH));   // one workgroup per pair of query blocks
-  const dim3 block(kAttnThreads);
+  hipLaunchKernelGGL((attn_fp8_e4m3<kPMode, kDump, kVF>), grid, dim3(kAttnThreads), 0, st, a);
+}
+
+template <int kPMode, int kVF>
+static void launch_pm(const AttnArgs& a, bool dump, hipStream_t st) {
+  if (dump) launch_one<kPMode, true, kVF>(a, st);
+  else launch_one<kPMode, false, kVF>(a, st);
+}
+
+static int launch_e4m3(const AttnArgs& a, int p_mode, bool dump, hipStream_t st, bool fp4 = false) {
   if (fp4) {
-    if (p_mode == VC_P_EXPCAST) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, false, VC_V_MXFP4>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, false, VC_V_MXFP4>), grid, block, 0, st, a);
-  } else if (p_mode == VC_P_EXPCAST) {
-    if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, true, VC_V_E4M3>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_EXPCAST, false, VC_V_E4M3>), grid, block, 0, st, a);
+    if (p_mode == VC_P_EXPCAST) launch_pm<VC_P_EXPCAST, VC_V_MXFP4>(a, dump, st);
+    else launch_pm<VC_P_FP32EXP_E4M3, VC_V_MXFP4>(a, dump, st);
   } else {
-    if (dump) hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, true, VC_V_E4M3>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_fp8_e4m3<VC_P_FP32EXP_E4M3, false, VC_V_E4M3>), grid, block, 0, st, a);
+    if (p_mode == VC_P_EXPCAST) launch_pm<VC_P_EXPCAST, VC_V_E4M3>(a, dump, st);
+    else launch_pm<VC_P_FP32EXP_E4M3, VC_V_E4M3>(a, dump, st);
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VC_OK : vc_set_hip_error((int)e);
@@ -538,7 +559,7 @@ using namespace vc;
 int vc_attn_nvfp4_launch(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
                          const float* k_scales, const uint8_t* v_codes, const float* v_scales,
                          const uint8_t* v_group_scales, const uint16_t* v_means, int B, int H, int N,
-                         float c0, float* out, hipStream_t st);
+                         float c0, float* out, float* s_dump, uint16_t* p_dump, hipStream_t st);
 
 extern "C" int vc_attn_fp8_fwd(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
                                const float* k_scales, const uint8_t* v_codes, const float* v_scales,
@@ -567,7 +588,37 @@ extern "C" int vc_attn_fp8_fwd(const uint8_t* q_codes, const float* q_scales, co
   if (v_format == VC_V_NVFP4 && p_mode == VC_P_FP32_BF16) {
     if (!v_group_scales) return VC_ERR_INVALID_ARG;
     return vc_attn_nvfp4_launch(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales,
-                                v_means, B, H, N, c0, out, st);
+                                v_means, B, H, N, c0, out, nullptr, nullptr, st);
+  }
+  return VC_ERR_UNSUPPORTED;
+}
+
+extern "C" int vc_attn_fwd_dump(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
+                                const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                                const uint8_t* v_group_scales, const uint16_t* v_means, int B, int H, int N, int d,
+                                float softmax_scale, int p_mode, int v_format, float* out, float* s_dump,
+                                void* p_dump, void* stream) {
+  if (d != kD) return VC_ERR_UNSUPPORTED;
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !v_means || !out || !s_dump ||
+      !p_dump)
+    return VC_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
+  const int nb = (N + kBlock - 1) / kBlock;
+  if ((long long)nb * B * H > 0x7FFFFFFFLL) return VC_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float c0 = score_scale_c0(softmax_scale);
+  const bool e4m3_p = p_mode == VC_P_EXPCAST || p_mode == VC_P_FP32EXP_E4M3;
+  if ((v_format == VC_V_E4M3 || v_format == VC_V_MXFP4) && e4m3_p) {
+    if (v_format == VC_V_MXFP4 && !v_group_scales) return VC_ERR_INVALID_ARG;
+    AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means,
+               v_format == VC_V_MXFP4 ? v_group_scales : nullptr, out, s_dump, static_cast<uint8_t*>(p_dump),
+               N, nb, B * H, c0};
+    return launch_e4m3(a, p_mode, true, st, v_format == VC_V_MXFP4);
+  }
+  if (v_format == VC_V_NVFP4 && p_mode == VC_P_FP32_BF16) {
+    if (!v_group_scales) return VC_ERR_INVALID_ARG;
+    return vc_attn_nvfp4_launch(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales,
+                                v_means, B, H, N, c0, out, s_dump, static_cast<uint16_t*>(p_dump), st);
   }
   return VC_ERR_UNSUPPORTED;
 }
@@ -576,14 +627,7 @@ extern "C" int vc_attn_fp8_fwd_dump(const uint8_t* q_codes, const float* q_scale
                                     const float* k_scales, const uint8_t* v_codes, const float* v_scales,
                                     const uint16_t* v_means, int B, int H, int N, int d, float softmax_scale,
                                     int p_mode, float* out, float* s_dump, uint8_t* p_dump, void* stream) {
-  if (d != kD) return VC_ERR_UNSUPPORTED;
   if (p_mode != VC_P_EXPCAST && p_mode != VC_P_FP32EXP_E4M3) return VC_ERR_UNSUPPORTED;
-  if (!q_codes || !q_scales || !k_codes || !k_scales || !v_codes || !v_scales || !v_means || !out || !s_dump ||
-      !p_dump)
-    return VC_ERR_INVALID_ARG;
-  if (B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
-  const int nb = (N + kBlock - 1) / kBlock;
-  AttnArgs a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_means, nullptr, out, s_dump, p_dump,
-             N, nb, B * H, score_scale_c0(softmax_scale)};
-  return launch_e4m3(a, p_mode, true, static_cast<hipStream_t>(stream));
+  return vc_attn_fwd_dump(q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, nullptr, v_means, B, H, N, d,
+                          softmax_scale, p_mode, VC_V_E4M3, out, s_dump, p_dump, stream);
 }

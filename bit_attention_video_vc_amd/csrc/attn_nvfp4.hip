@@ -28,6 +28,7 @@ struct N4Args {
   const uint8_t* gs;                    // E4M3 group scales [BH, Np/16, 128]
   const uint16_t* means;
   float* out;
+  float* sdump; uint16_t* pdump;        // test hook: scores and bf16 P bits [BH, N, Np] (or null)
   int N, nb, BH;
   float c0;
 };
@@ -43,6 +44,7 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t n) {
   return __uint_as_float(mag | ((n & 8u) << 28));
 }
 
+template <bool kDump>
 __global__ void __launch_bounds__(kN4Threads) attn_nvfp4_kernel(N4Args a) {
   __shared__ __align__(16) uint8_t Ks[kTile_];
   __shared__ __align__(16) uint8_t Vb[kD * kRowBf];    // dequantised V^T, bf16, swizzled
@@ -164,6 +166,9 @@ __global__ void __launch_bounds__(kN4Threads) attn_nvfp4_kernel(N4Args a) {
     abat *= alpha;
     mx = mx_new;
 
+    // keys at or beyond N (last tile only) get P = 0: their scores are -inf
+    // for the row max, and -inf * kap is NaN when kap = 0 (a zero Q or K block)
+    const int nvalid = min(N - t * kBlock, kBlock);
     float rsum = 0.0f;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -172,9 +177,21 @@ __global__ void __launch_bounds__(kN4Threads) attn_nvfp4_kernel(N4Args a) {
         uint32_t pw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(s[m][8 * s2 + 2 * e] * kap - mx_new);
-          const float p1 = __builtin_amdgcn_exp2f(s[m][8 * s2 + 2 * e + 1] * kap - mx_new);
+          const int key0 = 64 * (m >> 1) + 32 * g + 16 * (m & 1) + 8 * s2 + 2 * e;
+          float p0 = __builtin_amdgcn_exp2f(s[m][8 * s2 + 2 * e] * kap - mx_new);
+          float p1 = __builtin_amdgcn_exp2f(s[m][8 * s2 + 2 * e + 1] * kap - mx_new);
+          if (nvalid < kBlock) {
+            p0 = key0 < nvalid ? p0 : 0.0f;
+            p1 = key0 + 1 < nvalid ? p1 : 0.0f;
+          }
           const uint32_t b0 = f32_to_bf16_rne(p0), b1 = f32_to_bf16_rne(p1);
+          if (kDump && qrow < N) {
+            const long long idx = ((long long)bh * N + qrow) * Np + (long long)t * kBlock + key0;
+            a.sdump[idx] = key0 < nvalid ? s[m][8 * s2 + 2 * e] : 0.0f;
+            a.sdump[idx + 1] = key0 + 1 < nvalid ? s[m][8 * s2 + 2 * e + 1] : 0.0f;
+            a.pdump[idx] = (uint16_t)b0;
+            a.pdump[idx + 1] = (uint16_t)b1;
+          }
           rsum += __uint_as_float(b0 << 16) + __uint_as_float(b1 << 16);
           pw[e] = b0 | (b1 << 16);
         }
@@ -233,11 +250,13 @@ using namespace vc;
 int vc_attn_nvfp4_launch(const uint8_t* q_codes, const float* q_scales, const uint8_t* k_codes,
                          const float* k_scales, const uint8_t* v_codes, const float* v_scales,
                          const uint8_t* v_group_scales, const uint16_t* v_means, int B, int H, int N,
-                         float c0, float* out, hipStream_t st) {
+                         float c0, float* out, float* s_dump, uint16_t* p_dump, hipStream_t st) {
   const int nb = (N + kBlock - 1) / kBlock;
   N4Args a{q_codes, q_scales, k_codes, k_scales, v_codes, v_scales, v_group_scales, v_means, out,
-           N, nb, B * H, c0};
-  hipLaunchKernelGGL(attn_nvfp4_kernel, dim3((unsigned)(nb * B * H)), dim3(kN4Threads), 0, st, a);
+           s_dump, p_dump, N, nb, B * H, c0};
+  const dim3 grid((unsigned)(nb * B * H)), block(kN4Threads);
+  if (s_dump) hipLaunchKernelGGL(attn_nvfp4_kernel<true>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(attn_nvfp4_kernel<false>, grid, block, 0, st, a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VC_OK : vc_set_hip_error((int)e);
 }

@@ -1,0 +1,86 @@
+// Test hook: single gfx950 instructions on caller data.  The attention and
+// preprocessing kernels rest on a few facts about these instructions (the FP8
+// matrix instructions' accumulation, the rounding and range of the two byte
+// conversions, the accuracy of the hardware exp2); this entry point runs each
+// instruction alone so that tests can record those facts against exact
+// arithmetic on the host.
+#include "vc_common.h"
+
+namespace vc {
+
+// V_CVT_PK_FP8_F32 without the clamp the encoders apply (what = 0)
+__global__ void probe_cvt_fp8(const float* in, uint8_t* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(in[i], 0.0f, 0u, false) & 0xFFu);
+}
+
+// V_CVT_PK_U8_F32 (what = 1)
+__global__ void probe_cvt_u8(const float* in, uint8_t* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_u8_f32(in[i], 0, 0u) & 0xFFu);
+}
+
+// V_EXP_F32 (what = 2)
+__global__ void probe_exp2(const float* in, float* out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = __builtin_amdgcn_exp2f(in[i]);
+}
+
+// One wavefront per tile: D = A . B^T + C with V_MFMA_F32_32X32X64_F8F6F4 (what
+// = 3, M = N = 32, K = 64) or V_MFMA_F32_16X16X128_F8F6F4 (what = 4, M = N = 16,
+// K = 128), E4M3 operands.  Tile layout in `in`: A [M][K] bytes, B [N][K]
+// bytes, C [M][N] fp32; in `out`: D [M][N] fp32.  Lane l holds row (or column)
+// l % M and the K-slice 32 (l / M) .. 32 (l / M) + 31 of both operands.
+template <int M>
+__global__ void __launch_bounds__(64) probe_mfma(const uint8_t* in, float* out, int tiles) {
+  constexpr int K = 2048 / M;
+  constexpr int tile_bytes = 2 * M * K + 4 * M * M;
+  const int tile = blockIdx.x, l = threadIdx.x;
+  if (tile >= tiles) return;
+  const uint8_t* A = in + (long long)tile * tile_bytes;
+  const uint8_t* B = A + M * K;
+  const float* C = reinterpret_cast<const float*>(B + M * K);
+  float* D = out + (long long)tile * M * M;
+  const int r = l % M, kg = l / M;
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = *reinterpret_cast<const int*>(A + r * K + 32 * kg + 4 * i);
+    b[i] = *reinterpret_cast<const int*>(B + r * K + 32 * kg + 4 * i);
+  }
+  if constexpr (M == 32) {
+    v16f c;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = C[(8 * (i >> 2) + 4 * kg + (i & 3)) * M + r];
+    const v16f d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) D[(8 * (i >> 2) + 4 * kg + (i & 3)) * M + r] = d[i];
+  } else {
+    v4f c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = C[(4 * kg + i) * M + r];
+    const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) D[(4 * kg + i) * M + r] = d[i];
+  }
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" int vc_device_probe(int what, const void* in, void* out, int n, void* stream) {
+  if (!in || !out || n < 1) return VC_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  switch (what) {
+    case 0: hipLaunchKernelGGL(probe_cvt_fp8, grid, block, 0, st, (const float*)in, (uint8_t*)out, n); break;
+    case 1: hipLaunchKernelGGL(probe_cvt_u8, grid, block, 0, st, (const float*)in, (uint8_t*)out, n); break;
+    case 2: hipLaunchKernelGGL(probe_exp2, grid, block, 0, st, (const float*)in, (float*)out, n); break;
+    case 3: hipLaunchKernelGGL(probe_mfma<32>, dim3((unsigned)n), dim3(64), 0, st, (const uint8_t*)in, (float*)out, n); break;
+    case 4: hipLaunchKernelGGL(probe_mfma<16>, dim3((unsigned)n), dim3(64), 0, st, (const uint8_t*)in, (float*)out, n); break;
+    default: return VC_ERR_UNSUPPORTED;
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? VC_OK : vc_set_hip_error((int)e);
+}

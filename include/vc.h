@@ -225,6 +225,37 @@ int vc_attn_fp8_fwd_dump(const uint8_t* q_codes, const float* q_scales,
                          float* out, float* s_dump, uint8_t* p_dump, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Test hook for every attention pairing: vc_attn_fp8_fwd that also records,
+ * for every query row and every padded key slot, the fp32 score S and the P
+ * value the kernel fed to its P.V product.  p_dump holds u8 E4M3 codes
+ * [B,H,N,Np] for VC_P_EXPCAST / VC_P_FP32EXP_E4M3 (V in VC_V_E4M3 or
+ * VC_V_MXFP4) and uint16 bf16 bit patterns [B,H,N,Np] for VC_P_FP32_BF16 (V in
+ * VC_V_NVFP4).  s_dump fp32 [B,H,N,Np]; key index in permuted order; masked
+ * slots get S = 0, P = 0.  Other arguments, outputs and errors as in
+ * vc_attn_fp8_fwd.  Meant for small N (the dumps are N*Np per head).
+ * ------------------------------------------------------------------------ */
+int vc_attn_fwd_dump(const uint8_t* q_codes, const float* q_scales,
+                     const uint8_t* k_codes, const float* k_scales,
+                     const uint8_t* v_codes, const float* v_scales, const uint8_t* v_group_scales,
+                     const uint16_t* v_means, int B, int H, int N, int d, float softmax_scale,
+                     int p_mode, int v_format, float* out, float* s_dump, void* p_dump, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Test hook: one gfx950 instruction on caller data, so that tests can record
+ * the device facts the kernels rely on (element counts n; all device memory):
+ *   what 0  V_CVT_PK_FP8_F32, no clamp first   in fp32 [n] -> out u8 [n]
+ *   what 1  V_CVT_PK_U8_F32                     in fp32 [n] -> out u8 [n]
+ *   what 2  V_EXP_F32                           in fp32 [n] -> out fp32 [n]
+ *   what 3  V_MFMA_F32_32X32X64_F8F6F4, E4M3    n tiles: in = A u8 [32][64],
+ *           B u8 [32][64], C fp32 [32][32] per tile; out D fp32 [32][32] per
+ *           tile, D = A . B^T + C
+ *   what 4  V_MFMA_F32_16X16X128_F8F6F4, E4M3   the same with 16, 16, 128
+ * Returns VC_ERR_UNSUPPORTED for other `what`, VC_ERR_INVALID_ARG for null
+ * pointers or n < 1.
+ * ------------------------------------------------------------------------ */
+int vc_device_probe(int what, const void* in, void* out, int n, void* stream);
+
+/* ------------------------------------------------------------------------
  * Grouping cadence over a denoising trajectory (paper digest, clustering-
  * rationale paragraph and limitations; news article, "V-Smooth"; insight
  * article, "Value Is the Error Source Earlier Methods Underestimated"): grouping

@@ -547,9 +547,10 @@ def online_attention(Qd, Kd, Vres, means, N, qscale_rows, kscales, c0, p_mode, r
     mx = np.full(R, -np.inf)          # float64 holder; float32 values in the quantised modes
     l = np.zeros(R)
     U = np.zeros((R, d))
+    srows = None if scores is None else np.asarray(scores)[rows]
     for t in range(nb):
         k0, k1 = t * BLOCK, min(N, (t + 1) * BLOCK)
-        S64 = q @ Kd[k0:k1].T if scores is None else f32(scores[rows][:, k0:k1]).astype(np.float64)
+        S64 = q @ Kd[k0:k1].T if scores is None else f32(srows[:, k0:k1]).astype(np.float64)
         kap = f32(f32(sq * F32(kscales[t])) * F32(c0))
         if p_mode == "exact":          # no rounding anywhere (used to pin the algebra)
             x = S64 * kap.astype(np.float64)[:, None]

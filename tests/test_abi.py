@@ -89,3 +89,19 @@ def test_argument_errors_are_synchronous(L):
     assert L.vc_attn_bf16_fwd(p, p, p, 1, 1, 8, 128, 0.1, p, p, 16, null) == -3
     assert L.vc_attn_bf16_workspace(1, 2, 300, 128) == 2 * 3 * 128 * 256
     assert L.vc_attn_fp8_fwd_dump(*[p] * 7, 1, 1, 8, 128, 0.1, 2, p, p, p, null) == -2
+
+
+def test_test_hooks_reject_bad_arguments(L):
+    p = ctypes.c_void_p(16)
+    null = None
+    a = [p] * 8 + [1, 1, 8, 128, 0.1]
+    assert L.vc_attn_fwd_dump(*a, 0, 1, p, p, p, null) == -2          # ExpCast with NVFP4
+    assert L.vc_attn_fwd_dump(*a, 2, 0, p, p, p, null) == -2          # bf16 P with E4M3 V
+    assert L.vc_attn_fwd_dump(*a, 0, 0, p, null, p, null) == -1       # no score dump
+    a6 = [p] * 6 + [null, p] + [1, 1, 8, 128, 0.1]
+    assert L.vc_attn_fwd_dump(*a6, 0, 2, p, p, p, null) == -1         # MXFP4 needs its group scales
+    assert L.vc_attn_fwd_dump(*a6, 2, 1, p, p, p, null) == -1         # so does NVFP4
+    assert L.vc_attn_fwd_dump(*[p] * 8, 1, 1, 8, 64, 0.1, 0, 0, p, p, p, null) == -2
+    assert L.vc_device_probe(9, p, p, 4, null) == -2
+    assert L.vc_device_probe(0, p, p, 0, null) == -1
+    assert L.vc_device_probe(0, null, p, 4, null) == -1

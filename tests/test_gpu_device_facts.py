@@ -1,0 +1,135 @@
+"""Device facts the kernels rest on, recorded on the GPU through the
+vc_device_probe test hook against exact arithmetic on the host:
+
+- the FP8 matrix instructions (32x32x64 for Q.K and P.V, 16x16x128 for the row
+  sums) do not return the exactly rounded dot product: their fp32 result stays
+  within 2^-10 of the sum of |products| of the exact value (the bound the parity
+  tests use for the kernel's scores), so P bytes are compared given the
+  kernel's scores;
+- V_CVT_PK_FP8_F32 rounds to nearest even but does not saturate (|x| > 464
+  gives the NaN code), which is why every encoder clamps to +-448 first;
+- V_CVT_PK_U8_F32 rounds to nearest even and clamps to [0, 255] (the ExpCast
+  code conversion);
+- V_EXP_F32 is within one ulp of exp2 (the conventional P path's codes may move
+  one step at rounding boundaries).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+S_ERR_L1 = 2.0 ** -10
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def vc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_attention_video_vc_amd as vc
+    vc.lib()
+    return vc
+
+
+def _e4m3_values():
+    """float64 value of every finite E4M3 byte (NaN codes 0x7F / 0xFF excluded)."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    return codes, torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _probe(vc, what, x, out_dtype, n):
+    dev = torch.device("cuda:0")
+    inp = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    out = torch.empty(n if what < 3 else n * (1024 if what == 3 else 256), dtype=out_dtype, device=dev)
+    vc.device_probe(["cvt_fp8", "cvt_u8", "exp2", "mfma_32x32x64", "mfma_16x16x128"][what], inp, out, n)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("what,M,K", [(3, 32, 64), (4, 16, 128)])
+@pytest.mark.parametrize("with_c", [False, True])
+def test_fp8_matrix_instruction_accumulation(vc, what, M, K, with_c):
+    """Random finite E4M3 operands over the whole range (and a random fp32 C):
+    D against the exact A.B^T + C (exact in float64: products are multiples of
+    2^-18 below 2^18)."""
+    rng = np.random.default_rng(what * 10 + with_c)
+    codes, vals = _e4m3_values()
+    tiles = 64
+    ia = rng.integers(0, len(codes), (tiles, M, K))
+    ib = rng.integers(0, len(codes), (tiles, M, K))
+    C = (rng.standard_normal((tiles, M, M)) * 1e3).astype(np.float32) if with_c else np.zeros((tiles, M, M), np.float32)
+    buf = np.concatenate([np.concatenate([codes[ia[t]].ravel(), codes[ib[t]].ravel(),
+                                          C[t].ravel().view(np.uint8)]) for t in range(tiles)])
+    D = _probe(vc, what, buf, torch.float32, tiles).reshape(tiles, M, M)
+    A, B = vals[ia], vals[ib]
+    exact = np.einsum("tik,tjk->tij", A, B) + C.astype(np.float64)
+    l1 = np.einsum("tik,tjk->tij", np.abs(A), np.abs(B)) + np.abs(C.astype(np.float64))
+    err = np.abs(D.astype(np.float64) - exact) / np.maximum(l1, 1e-30)
+    rne = float((D == exact.astype(np.float32)).mean())
+    _say(f"MFMA {M}x{M}x{K}, C {'random' if with_c else 'zero'}: D == RNE(exact) on {rne:.4f} of elements; "
+         f"max |D - exact| / sum|products| = {err.max():.2e}")
+    assert np.isfinite(D).all()
+    assert err.max() <= S_ERR_L1
+
+
+def test_fp8_matrix_instruction_small_integers_are_exact(vc):
+    """Operands that are small integers (every partial sum an integer below
+    2^24): the result is exact, so the inexactness above is a rounding of the
+    accumulation, not a wrong product."""
+    rng = np.random.default_rng(5)
+    codes, vals = _e4m3_values()
+    small = np.nonzero((np.abs(vals) <= 8) & (vals == np.round(vals)))[0]
+    tiles = 16
+    ia = rng.choice(small, (tiles, 32, 64))
+    ib = rng.choice(small, (tiles, 32, 64))
+    C = np.zeros((tiles, 32, 32), np.float32)
+    buf = np.concatenate([np.concatenate([codes[ia[t]].ravel(), codes[ib[t]].ravel(), C[t].ravel().view(np.uint8)])
+                          for t in range(tiles)])
+    D = _probe(vc, 3, buf, torch.float32, tiles).reshape(tiles, 32, 32)
+    exact = np.einsum("tik,tjk->tij", vals[ia], vals[ib])
+    np.testing.assert_array_equal(D.astype(np.float64), exact)
+
+
+def test_fp8_conversion_rounds_to_nearest_even_without_saturation(vc):
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.uniform(-463.9, 463.9, 1 << 18), rng.standard_normal(1 << 16) * 2 ** -7,
+                        np.float32([448.0, 463.99, -463.99, 0.0, -0.0, 2 ** -10, 3 * 2 ** -11])]).astype(np.float32)
+    got = _probe(vc, 0, x, torch.uint8, len(x))
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, want)
+    # 464 is the tie between 448 and the next step (480, not a finite E4M3FN
+    # value): ties to even give 448; anything above converts to the NaN code
+    edge = np.float32([464.0, -464.0])
+    assert list(_probe(vc, 0, edge, torch.uint8, 2)) == [0x7E, 0xFE]
+    big = np.float32([np.nextafter(np.float32(464), np.float32(1e9)), 465.0, -500.0, 1e30, -1e30, np.inf])
+    gb = _probe(vc, 0, big, torch.uint8, len(big))
+    _say(f"V_CVT_PK_FP8_F32 of {big.tolist()} -> {[hex(v) for v in gb]}")
+    assert np.all(gb & 0x7F == 0x7F), "no saturation: |x| > 464 converts to the NaN code"
+
+
+def test_u8_conversion_rounds_to_nearest_even_and_clamps(vc):
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.uniform(-300, 600, 1 << 18), np.arange(-10, 270, 0.5),
+                        np.float32([-0.0, 255.5, 256.0, 1e30, -1e30, -np.inf, np.inf])]).astype(np.float32)
+    got = _probe(vc, 1, x, torch.uint8, len(x))
+    want = np.clip(np.rint(x.astype(np.float64)), 0, 255).astype(np.uint8)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_exp2_is_within_one_ulp(vc):
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.uniform(-126, 0, 1 << 20), rng.uniform(-20, 20, 1 << 16),
+                        np.float32([0.0, -1.0, -0.5, 1.0])]).astype(np.float32)
+    got = _probe(vc, 2, x, torch.float32, len(x))
+    want = np.exp2(x.astype(np.float64)).astype(np.float32)
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    _say(f"V_EXP_F32: {float((ulps > 0).mean()):.2e} of results off the correctly rounded exp2, max {ulps.max()} ulp")
+    assert ulps.max() <= 1

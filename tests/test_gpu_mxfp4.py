@@ -1,10 +1,9 @@
 """GPU parity of the MXFP4 4-bit path: V residual as E2M1 values with one E8M0
 scale per 32 rows, fed to the block-scaled FP4 MFMA (P in E4M3, by ExpCast or
 by fp32 exp2 + convert).  Codes and scales bit-exact against the oracle; the
-output within 1e-4 of the oracle replayed on the kernel's own scores (the
-scores come from the E4M3-path dump of the same Q/K codes: the Q.K part of the
-kernel does not depend on the V format), and within the Gaussian-QK tolerance
-of the oracle on exact scores."""
+output within 1e-4 of the oracle replayed on the kernel's own scores, P bytes
+bit-exact given them (ExpCast), and within the Gaussian-QK tolerance of the
+oracle on exact scores."""
 import math
 import sys
 
@@ -13,6 +12,7 @@ import pytest
 import torch
 
 from oracle import oracle as O
+from tests import test_gpu_parity as GP
 import vc_workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -59,18 +59,12 @@ def _check(vc, Q, K, V, k, iters, heads, rows=None):
     Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
     perm, _, _ = vc.vsmooth_group(Vd, k, iters)
     prep = vc.preprocess_quant(Qd, Kd, Vd, perm, "mxfp4")
-    prep8 = vc.preprocess_quant(Qd, Kd, Vd, perm, "e4m3")
     torch.cuda.synchronize()
     q16, k16, v16 = _u16(Q), _u16(K), _u16(V)
     perm_c = perm.cpu().numpy()
     N = Q.shape[2]
     outs = {pm: vc.attn_fp8_fwd(prep, SCALE, pm).cpu().numpy() for pm in ("expcast", "fp32exp_e4m3")}
-    small = N <= 2048
-    dumps = {}
-    if small:
-        for pm in ("expcast", "fp32exp_e4m3"):
-            _, S, _ = vc.attn_fp8_fwd_dump(prep8, SCALE, pm)
-            dumps[pm] = S.cpu().numpy()
+    preps = {}
     for (b, h) in heads:
         pr = O.preprocess_head(q16[b, h], k16[b, h], v16[b, h], perm_c[b, h].astype(np.int64), "mxfp4")
         np.testing.assert_array_equal(prep["k_codes"][b, h].cpu().numpy(), pr["k_codes"], err_msg="k codes")
@@ -86,11 +80,10 @@ def _check(vc, Q, K, V, k, iters, heads, rows=None):
             e = O.rel_l2(got, ref)
             _say(f"  b{b} h{h} {pm}: rel-L2 vs exact-score oracle {e:.2e}")
             assert e <= TOL_GAUSS_QK
-            if small:
-                ref_s = O.vc_attention_head(pr, SCALE, pm, scores=dumps[pm][b, h])
-                e2 = O.rel_l2(outs[pm][b, h], ref_s)
-                _say(f"  b{b} h{h} {pm}: rel-L2 vs oracle on the kernel's scores {e2:.2e}")
-                assert e2 <= TOL_GIVEN_S
+        preps[(b, h)] = pr
+    # P bytes given the MXFP4 kernel's own scores, output replayed on them (1e-4)
+    for pm in ("expcast", "fp32exp_e4m3"):
+        GP._check_given_scores(vc, prep, preps, pm, rows, report_e2e=True)
 
 
 # N = 600: five 128-row blocks, one full four-block mean-restore batch and one more

@@ -108,43 +108,101 @@ def _check_attention(vc, prep, preps, p_mode, rows_per_head=None, tol=TOL_OUT):
     return out, max(errs)
 
 
-def _check_given_scores(vc, prep, preps, p_mode):
-    """Dump the kernel's scores and P bytes: P bit-exact given S, scores within
-    the FP8 accumulation bound, output equal to the oracle replayed on S."""
-    out, S, P = vc.attn_fp8_fwd_dump(prep, SCALE, p_mode)
-    out, S, P = out.cpu().numpy(), S.cpu().numpy(), P.cpu().numpy()
+def _head_prep(prep, b, h):
+    """The preprocessed tensors of one (batch, head) as a B = H = 1 problem
+    (views into the same memory), so that a score dump holds one head only."""
+    sub = dict(prep, B=1, H=1)
+    for k, v in prep.items():
+        if isinstance(v, torch.Tensor):
+            sub[k] = v[b:b + 1, h:h + 1]
+    return sub
+
+
+def _p_steps(got, want, p_mode):
+    """Distance in format steps between two P tiles: E4M3 codes are positive
+    bytes whose integer order is the value order; bf16 P bits likewise."""
+    return np.abs(got.astype(np.int64) - want.astype(np.int64))
+
+
+def _check_given_scores(vc, prep, preps, p_mode, rows=None, report_e2e=False):
+    """Dump the kernel's scores and P values (vc_attn_fwd_dump): P bit-exact
+    given S for ExpCast (one fmaf and a rounding), within one step for the paths
+    through the hardware exp2 (within 1 ulp of exp2); scores within the FP8
+    accumulation bound; output equal to the oracle replayed on S (rel-L2 1e-4).
+    With report_e2e, also the end-to-end P mismatch against the exact-score
+    oracle: rate, largest step, and flips across the flush boundary
+    (a code 8 on one side and 0 on the other).  Returns the per-head stats."""
+    stats = {}
     for (b, h), pr in preps.items():
+        out, S, P = vc.attn_fwd_dump(_head_prep(prep, b, h), SCALE, p_mode)
+        torch.cuda.synchronize()
         N = pr["N"]
         nb = O.n_blocks(N)
+        Np = nb * 128
+        rws = np.arange(N) if rows is None else np.asarray(rows)
+        ridx = torch.from_numpy(rws).to(S.device)
+        S_rows = S[0, 0].index_select(0, ridx).cpu().numpy()
+        P_rows = P[0, 0].index_select(0, ridx).cpu().numpy()
+        if p_mode == "fp32_bf16":
+            P_rows = P_rows.view(np.uint16)
+        out_rows = out[0, 0].index_select(0, ridx).cpu().numpy()
+        del out, S, P
+        S_full = np.zeros((N, Np), np.float32)      # untouched pages stay unallocated
+        S_full[rws] = S_rows
         rec = []
-        O.vc_attention_head(pr, SCALE, p_mode, scores=S[b, h], record=rec)
-        mism = 0
+        ref_s = O.vc_attention_head(pr, SCALE, p_mode, rows=rws, scores=S_full, record=rec)
+        off = 0
         for t, r in enumerate(rec):
             k1 = r["codes"].shape[1]
-            got = P[b, h][:, t * 128:t * 128 + k1]
+            got = P_rows[:, t * 128:t * 128 + k1]
             if p_mode == "expcast":   # one fmaf + RNE: bit-exact given S
-                np.testing.assert_array_equal(got, r["codes"], err_msg=f"P bytes given S, b{b} h{h} tile {t}")
-            else:                     # hardware exp2 is within 1 ulp: codes may move one step at boundaries
-                d = np.abs(got.astype(int) - r["codes"].astype(int))
-                assert d.max() <= 1
-                mism += int((d > 0).sum())
-            assert not P[b, h][:, t * 128 + k1:(t + 1) * 128].any()
+                np.testing.assert_array_equal(got, r["codes"], err_msg=f"P given S, b{b} h{h} tile {t}")
+            else:                     # hardware exp2 is within 1 ulp: P may move one step at boundaries
+                d = _p_steps(got, r["codes"], p_mode)
+                assert d.max() <= 1, f"P given S off by {d.max()} steps, b{b} h{h} tile {t}"
+                off += int((d > 0).sum())
+            assert not P_rows[:, t * 128 + k1:(t + 1) * 128].any()
         if p_mode != "expcast":
-            rate = mism / float(N * N)
-            _say(f"  b{b} h{h} {p_mode}: P bytes off by one step given S: rate {rate:.1e}")
+            rate = off / float(len(rws) * N)
+            _say(f"  b{b} h{h} {p_mode}: P off by one step given S: rate {rate:.1e}")
             assert rate <= 1e-4
-        Qd = O.e4m3_decode(pr["q_codes"][:N])
-        Kd = O.e4m3_decode(pr["k_codes"][:nb * 128])
+        Qd = O.e4m3_decode(pr["q_codes"][rws])
+        Kd = O.e4m3_decode(pr["k_codes"][:N])
         exact = Qd @ Kd.T
         l1 = np.abs(Qd) @ np.abs(Kd).T
-        dS = np.abs(S[b, h].astype(np.float64) - exact)[:, :N]
-        worst = float((dS / np.maximum(l1[:, :N], 1e-30)).max())
-        _say(f"  b{b} h{h} {p_mode}: max |S - exact| / L1 = {worst:.2e}")
+        dS = np.abs(S_rows[:, :N].astype(np.float64) - exact)
+        worst = float((dS / np.maximum(l1, 1e-30)).max())
+        rne = float((S_rows[:, :N] == exact.astype(np.float32)).mean())
+        _say(f"  b{b} h{h} {p_mode}: max |S - exact| / L1 = {worst:.2e}; S == RNE(exact) on {rne:.4f}")
         assert worst <= S_ERR_L1
-        ref_s = O.vc_attention_head(pr, SCALE, p_mode, scores=S[b, h])
-        e = O.rel_l2(out[b, h], ref_s)
+        e = O.rel_l2(out_rows, ref_s)
         _say(f"  b{b} h{h} {p_mode}: output rel-L2 vs oracle on the kernel's scores {e:.2e}")
         assert e <= TOL_GIVEN_S
+        assert np.isfinite(out_rows).all()
+        st = dict(replay_rel_l2=e, s_err_l1=worst, s_rne_frac=rne)
+        if report_e2e:
+            rec_x = []
+            ref_x = O.vc_attention_head(pr, SCALE, p_mode, rows=rws, record=rec_x)
+            n_diff = n_flush = 0
+            dmax = 0
+            for t, r in enumerate(rec_x):
+                k1 = r["codes"].shape[1]
+                got = P_rows[:, t * 128:t * 128 + k1]
+                d = _p_steps(got, r["codes"], p_mode)
+                if p_mode != "fp32_bf16":
+                    fl = ((got == 0) & (r["codes"] >= 8)) | ((got >= 8) & (r["codes"] == 0))
+                    n_flush += int(fl.sum())
+                    d = np.where(fl, 0, d)
+                n_diff += int((d > 0).sum())
+                dmax = max(dmax, int(d.max()))
+            tot = float(len(rws) * N)
+            e2e = O.rel_l2(out_rows, ref_x)
+            _say(f"  b{b} h{h} {p_mode}: end to end vs exact-score oracle: P differs on {n_diff / tot:.2e} "
+                 f"(max {dmax} step), flush-boundary flips {n_flush / tot:.2e}, output rel-L2 {e2e:.2e}")
+            assert dmax <= 1
+            st.update(p_mismatch=n_diff / tot, flush_flips=n_flush / tot, e2e_rel_l2=e2e)
+        stats[(b, h)] = st
+    return stats
 
 
 def test_tiny_8bit_end_to_end(vc):
@@ -152,12 +210,17 @@ def test_tiny_8bit_end_to_end(vc):
     c = W.WORKLOADS["tiny-8bit"]
     Q, K, V = W.make_inputs("tiny-8bit")
     prep, preps, _ = _check_group_and_codes(vc, Q, K, V, c["k"], c["iters"])
-    _check_given_scores(vc, prep, preps, "expcast")
-    _check_given_scores(vc, prep, preps, "fp32exp_e4m3")
+    _check_given_scores(vc, prep, preps, "expcast", report_e2e=True)
+    _check_given_scores(vc, prep, preps, "fp32exp_e4m3", report_e2e=True)
     _check_attention(vc, prep, preps, "expcast", tol=TOL_GAUSS_QK)
 
 
 def test_expcast_ablation_both_p_paths(vc):
+    """The ExpCast ablation at its full shape (B1 H8 N8192, k32 T10, one cached
+    permutation for both P paths): codes of two heads in full, then on 227
+    sampled query rows of each the P bytes given the kernel's scores, the
+    output replayed on those scores, and the end-to-end P mismatch and output
+    error against the exact-score oracle."""
     _say("ExpCast ablation: B1 H8 N8192 k32 T10, conventional and ExpCast P paths")
     c = W.WORKLOADS["expcast-ablation"]
     Q, K, V = W.make_inputs("expcast-ablation")
@@ -166,6 +229,8 @@ def test_expcast_ablation_both_p_paths(vc):
     rows = np.concatenate([np.arange(0, 8192, 61), np.arange(8100, 8192)])
     _check_attention(vc, prep, preps, "fp32exp_e4m3", rows, tol=TOL_GAUSS_QK)
     _check_attention(vc, prep, preps, "expcast", rows, tol=TOL_GAUSS_QK)
+    _check_given_scores(vc, prep, preps, "expcast", rows, report_e2e=True)
+    _check_given_scores(vc, prep, preps, "fp32exp_e4m3", rows, report_e2e=True)
 
 
 def test_expcast_ablation_recipe_given_scores(vc):
@@ -286,6 +351,7 @@ def test_nvfp4_small_ragged(vc):
     _say("4-bit path: B1 H2 N1000 k8 T4, NVFP4 residual, fp32 softmax, bf16 P")
     Q, K, V = W.custom_inputs(1, 2, 1000, seed=41, recipe="clustered")
     prep, preps, _ = _check_group_and_codes(vc, Q, K, V, 8, 4, fmt="nvfp4")
+    _check_given_scores(vc, prep, preps, "fp32_bf16", report_e2e=True)
     _check_attention(vc, prep, preps, "fp32_bf16", tol=TOL_GAUSS_QK)
 
 
@@ -300,3 +366,58 @@ def test_ragged_4bit_sampled(vc):
     prep, preps, _ = _check_group_and_codes(vc, Q, K, V, c["k"], c["iters"], heads=heads, fmt="nvfp4")
     rows = np.concatenate([np.arange(0, 32760, 701), np.arange(32750, 32760)])
     _check_attention(vc, prep, preps, "fp32_bf16", rows, tol=TOL_GAUSS_QK)
+    # bf16 P given the kernel's scores, output replayed on them (1e-4), and the
+    # end-to-end P mismatch, on the same sampled rows of the two heads
+    _check_given_scores(vc, prep, preps, "fp32_bf16", rows, report_e2e=True)
+
+
+@pytest.mark.parametrize("fmt,p_mode", [("e4m3", "expcast"), ("e4m3", "fp32exp_e4m3"), ("mxfp4", "expcast"),
+                                        ("mxfp4", "fp32exp_e4m3"), ("nvfp4", "fp32_bf16")])
+def test_masked_keys_with_zero_scale_blocks(vc, fmt, p_mode):
+    """Ragged N with an all-zero Q block and an all-zero last K block: their
+    scales are 0, so the score scale kap is 0 for those tiles, and the keys past
+    N in the last tile must still take no part (no NaN from -inf * 0)."""
+    _say(f"masked keys, zero-scale blocks: B1 H1 N300, {fmt} / {p_mode}")
+    N = 300
+    Q, K, V = W.custom_inputs(1, 1, N, seed=77, recipe="clustered")
+    Q[:, :, 128:256] = 0
+    K[:, :, 256:300] = 0        # identity permutation: this is the last permuted K block
+    dev = torch.device("cuda:0")
+    perm = torch.arange(N, dtype=torch.int32, device=dev).reshape(1, 1, N)
+    prep = vc.preprocess_quant(Q.to(dev), K.to(dev), V.to(dev), perm, fmt)
+    torch.cuda.synchronize()
+    assert prep["q_scales"][0, 0, 1].item() == 0.0 and prep["k_scales"][0, 0, 2].item() == 0.0
+    pr = O.preprocess_head(_u16(Q[0, 0]), _u16(K[0, 0]), _u16(V[0, 0]), np.arange(N, dtype=np.int32), fmt)
+    out = vc.attn_fp8_fwd(prep, SCALE, p_mode).cpu().numpy()[0, 0]
+    assert np.isfinite(out).all()
+    e = O.rel_l2(out, O.vc_attention_head(pr, SCALE, p_mode))
+    _say(f"  output rel-L2 vs exact-score oracle {e:.2e}")
+    assert e <= TOL_GAUSS_QK
+    _check_given_scores(vc, prep, {(0, 0): pr}, p_mode, report_e2e=True)
+
+
+def test_preprocess_quant_entry_point_itself(vc):
+    """vc_preprocess_quant (no RoPE, no Hadamard) called through the C ABI
+    directly: every output bit-identical to the _ex call the binding makes,
+    which the other tests hold to the oracle bit for bit."""
+    import ctypes
+    _say("vc_preprocess_quant called directly: B1 H2 N1000 k8 T4, E4M3")
+    Q, K, V = W.custom_inputs(1, 2, 1000, seed=52, recipe="clustered")
+    prep_ex, preps, (Qd, Kd, Vd) = _check_group_and_codes(vc, Q, K, V, 8, 4)
+    perm, _, _ = vc.vsmooth_group(Vd, 8, 4)
+    direct = {k: torch.full_like(v, 0x5A if v.dtype == torch.uint8 else 7) for k, v in prep_ex.items()
+              if isinstance(v, torch.Tensor)}
+    L = vc.lib()
+    ws_bytes = L.vc_preprocess_workspace(1, 2, 1000, 128, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=Qd.device)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    rc = L.vc_preprocess_quant(P(Qd), P(Kd), P(Vd), P(perm), 1, 2, 1000, 128, 0,
+                               P(direct["q_codes"]), P(direct["q_scales"]), P(direct["k_codes"]),
+                               P(direct["k_scales"]), P(direct["v_codes"]), P(direct["v_scales"]), None,
+                               P(direct["v_means"]), P(ws), ws_bytes,
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert set(direct) == {"q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales", "v_means"}
+    for k, v in direct.items():
+        assert torch.equal(v, prep_ex[k]), k
