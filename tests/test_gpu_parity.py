@@ -2,13 +2,23 @@
 element, on seeded inputs (tiny configuration, the ExpCast ablation, ragged and
 degenerate shapes, and sampled outputs of the full Wan2.2-shaped run).
 
-Bar: bit-exact for labels, permutations, means, scales and every code byte;
-P bytes bit-exact given the kernel's own scores (the FP8 MFMA does not return
-the exactly rounded dot product, so scores are checked against a bound and the
-oracle is also replayed on the kernel's scores); fp32 outputs within relative L2
-1e-4 of the oracle replayed on the kernel's scores, and within 1e-3 of the
-exact-score oracle on the Wan2.2 shape (6e-3 on the Gaussian-Q/K shapes, where
-score rounding flips more P codes)."""
+Bar: bit-exact for labels, permutations, means, scales and every code byte.
+The FP8 matrix instructions do not return the exactly rounded dot product (each
+group of 8 products keeps 13 bits below its largest exponent; see
+test_gpu_device_facts.py), so the kernel's scores differ from the oracle's
+exact ones by up to 2^-10 of the sum of |products| (measured: 1e-5 to 5e-4).
+Hence the P contract: P bit-exact GIVEN the kernel's scores (ExpCast; the
+exp2 paths within one step at a rate <= 1e-4), and the output within relative
+L2 1e-4 of the oracle replayed on those scores.
+
+End to end against the exact-score oracle the score differences flip about one
+P code in 5,000-50,000 (never by more than one step), and the benchmark spec bar of
+rel-L2 <= 1e-3 holds on the Wan2.2 shape (measured 1.6e-4 to 1.8e-4) and on the
+ragged 4-bit workload (3.4e-5 to 3.5e-5) but NOT on the N(0,1) / outlier Q,K
+shapes of the tiny and ExpCast-ablation workloads (measured 1.1e-3 to 3.2e-3:
+near-uniform attention rows whose output is much smaller than V, so a few
+flipped codes show).  Those are held to 6e-3 end to end and to the given-S bar
+above, and the mismatch rates are printed."""
 import math
 import sys
 
