@@ -49,8 +49,10 @@ def lib():
         L.vc_attn_fp8_fwd_dump.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, P, P]
         L.vc_attn_fwd_dump.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, P, P, P]
         L.vc_device_probe.argtypes = [I, P, P, I, P]
+        L.vc_preprocess_quant_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        L.vc_preprocess_noalloc_max_scratch.restype = Z
         for f in ("vc_vsmooth_group", "vc_preprocess_quant", "vc_preprocess_quant_ex", "vc_attn_fp8_fwd", "vc_attn_bf16_fwd",
-                  "vc_attn_fp8_fwd_dump", "vc_attn_fwd_dump", "vc_device_probe"):
+                  "vc_attn_fp8_fwd_dump", "vc_attn_fwd_dump", "vc_device_probe", "vc_preprocess_quant_noalloc"):
             getattr(L, f).restype = I
         for f in ("vc_group_due", "vc_group_source"):
             getattr(L, f).argtypes = [I, I, I, F]

@@ -21,6 +21,7 @@ extern "C" const char* vc_status_string(int status) {
     case VC_ERR_UNSUPPORTED: return "unsupported shape or mode";
     case VC_ERR_WORKSPACE: return "workspace missing or too small";
     case VC_ERR_HIP: return hipGetErrorString(static_cast<hipError_t>(g_last_hip_error));
+    case VC_ERR_SCRATCH: return "problem too large for the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

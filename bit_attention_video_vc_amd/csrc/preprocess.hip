@@ -21,6 +21,8 @@
 //          per block (channel-major), the operand order of the attention kernel.
 // A small clear kernel zeroes the amax accumulators first (no memset on the
 // stream, so the sequence can be captured in a graph).
+#include <mutex>
+
 #include "vc_common.h"
 
 namespace vc {
@@ -370,6 +372,56 @@ extern "C" int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, cons
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return vc_set_hip_error((int)e);
   return VC_OK;
+}
+
+// Scratch of the allocation-free entry point: the amax accumulators live in a
+// file-scope device array (one copy per GPU, held until the process ends)
+// instead of a caller workspace.  On the host `scratch` only names the symbol;
+// its device address comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kScratchBytes = 1u << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr and a recorded
+// HIP error if the lookup fails).
+void* scratch_on_current_device() {
+  int dev = 0;
+  const hipError_t ed = hipGetDevice(&dev);
+  if (ed != hipSuccess) { vc_set_hip_error((int)ed); return nullptr; }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) { vc_set_hip_error((int)e); return nullptr; }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" size_t vc_preprocess_noalloc_max_scratch(void) { return kScratchBytes; }
+
+extern "C" int vc_preprocess_quant_noalloc(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                           const int32_t* perm, int B, int H, int N, int d, int v_format,
+                                           uint8_t* q_codes, float* q_scales, uint8_t* k_codes, float* k_scales,
+                                           uint8_t* v_codes, float* v_scales, uint8_t* v_group_scales,
+                                           uint16_t* v_means, void* stream) {
+  if (d != kD) return VC_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
+  const size_t need = vc_preprocess_workspace(B, H, N, d, v_format);
+  if (need > kScratchBytes) return VC_ERR_SCRATCH;
+  if (v_format != VC_V_E4M3 && v_format != VC_V_NVFP4 && v_format != VC_V_MXFP4) return VC_ERR_UNSUPPORTED;
+  if (!K || !V || !perm || !k_codes || !k_scales || !v_codes || !v_scales || !v_means) return VC_ERR_INVALID_ARG;
+  void* ws = scratch_on_current_device();
+  if (!ws) return VC_ERR_HIP;
+  // the clear kernel inside zeroes the accumulators first on every call
+  return vc_preprocess_quant_ex(Q, K, V, perm, B, H, N, d, v_format, nullptr, 0, q_codes, q_scales, k_codes,
+                                k_scales, v_codes, v_scales, v_group_scales, v_means, ws, kScratchBytes, stream);
 }
 
 extern "C" int vc_preprocess_quant(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,

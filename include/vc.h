@@ -50,7 +50,8 @@ enum vc_status {
   VC_ERR_INVALID_ARG = -1, /* null required pointer, N < 1, B/H < 1, k out of [1,256], iters < 1 */
   VC_ERR_UNSUPPORTED = -2, /* d != 128, unknown p_mode / v_format, or a mode pairing not built */
   VC_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than the *_workspace() size */
-  VC_ERR_HIP = -4          /* a HIP launch failed; see vc_last_hip_error() */
+  VC_ERR_HIP = -4,         /* a HIP launch failed; see vc_last_hip_error() */
+  VC_ERR_SCRATCH = -5      /* problem too large for the fixed scratch of an allocation-free entry point */
 };
 
 /* How the P tile (softmax numerator) is produced inside the attention kernel. */
@@ -141,6 +142,25 @@ int vc_preprocess_quant(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                         uint8_t* q_codes, float* q_scales, uint8_t* k_codes, float* k_scales,
                         uint8_t* v_codes, float* v_scales, uint8_t* v_group_scales,
                         uint16_t* v_means, void* workspace, size_t workspace_bytes, void* stream);
+
+/* vc_preprocess_quant for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and outputs, with no workspace argument.  Its scratch (the
+ * residual amax accumulators, vc_preprocess_workspace() bytes) lives in a
+ * fixed device array of vc_preprocess_noalloc_max_scratch() = 1 MiB per GPU,
+ * reserved by the library for the life of the process and cleared by every
+ * call; so B*H <= 2048 for VC_V_E4M3 / VC_V_MXFP4 (VC_V_NVFP4 needs B*H floats
+ * only), else VC_ERR_SCRATCH (checked before anything is enqueued).  The
+ * first call on a device looks up the array's address on that device (no
+ * allocation).  Every call on one GPU shares that array: calls that overlap in
+ * time on one GPU (different streams or threads) race and must be serialised
+ * by the caller.  Other arguments, outputs and errors as in vc_preprocess_quant. */
+size_t vc_preprocess_noalloc_max_scratch(void);
+int vc_preprocess_quant_noalloc(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                int B, int H, int N, int d, int v_format,
+                                uint8_t* q_codes, float* q_scales, uint8_t* k_codes, float* k_scales,
+                                uint8_t* v_codes, float* v_scales, uint8_t* v_group_scales,
+                                uint16_t* v_means, void* stream);
 
 /* vc_preprocess_quant with the two Q/K steps the pages also fuse into the
  * quantisation kernel (paper digest, preprocessing paragraph: RoPE and a

@@ -105,3 +105,17 @@ def test_test_hooks_reject_bad_arguments(L):
     assert L.vc_device_probe(9, p, p, 4, null) == -2
     assert L.vc_device_probe(0, p, p, 0, null) == -1
     assert L.vc_device_probe(0, null, p, 4, null) == -1
+
+
+def test_allocation_free_preprocessing_rejects_problems_beyond_its_scratch(L):
+    p = ctypes.c_void_p(16)
+    null = None
+    outs = [p, p, p, p, p, p, null, p]
+    assert L.vc_preprocess_noalloc_max_scratch() == 1 << 20
+    # E4M3 needs B*H*128 floats: 2049 heads exceed 1 MiB; checked before any GPU call
+    assert L.vc_preprocess_quant_noalloc(p, p, p, p, 1, 2049, 8, 128, 0, *outs, null) == -5
+    assert L.vc_preprocess_quant_noalloc(p, p, p, p, 3, 700, 8, 128, 2, *outs, null) == -5
+    assert L.vc_preprocess_quant_noalloc(p, p, p, p, 1, 1, 8, 96, 0, *outs, null) == -2
+    assert L.vc_preprocess_quant_noalloc(p, null, p, p, 1, 1, 8, 128, 0, *outs, null) == -1
+    assert L.vc_preprocess_quant_noalloc(p, p, p, p, 1, 1, 8, 128, 7, *outs, null) == -2
+    assert b"scratch" in L.vc_status_string(-5)
