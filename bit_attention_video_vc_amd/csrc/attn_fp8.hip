@@ -27,15 +27,18 @@
 //    block means are restored four blocks at a time, U += sum_t rowsum_t (x)
 //    mean_t / sv, by one bf16 MFMA per 32 channels with each factor split into
 //    a bf16 pair (relative error below 2^-16), so no VALU instruction touches
-//    the accumulators except the (rare) rescale when a running max moves.  A
-//    tile's row sum is consumed at the start of the next tile, so no wavefront
-//    waits for its P.V MFMAs before the tile's barrier.
-//  * tiles are copied global -> LDS through buffer resources, the next tile's
-//    copies issued between the Q.K MFMAs (not all at the start of a tile, where
-//    the eight wavefronts would queue behind each other in the address unit);
-//    the Q block scale is scalar and the next K block scale is prefetched at
-//    the start of the tile, so no wait for a copy sits inside a tile; the row
-//    max crosses the two 32-lane halves with V_PERMLANE32_SWAP (no LDS).
+//    the accumulators except the rescale when a running max moves.
+//  * software pipeline inside each wavefront: the Q.K MFMAs of tile t run
+//    beside the flush of tile t-1's P bytes and tile t's block maxima; tile t's
+//    ExpCast bytes (one fmaf + one byte conversion per score) run beside the
+//    P.V and row-sum MFMAs of tile t-1.  V is copied one tile behind K, so two
+//    LDS buffers of each suffice; operand reads run two MFMAs ahead; the
+//    rescale of the accumulators is deferred one step so that it never waits
+//    for MFMAs still in flight.
+//  * tiles are copied global -> LDS through buffer resources, issued between
+//    the Q.K MFMAs; the Q block scale is scalar and the next K block scale is
+//    prefetched at the start of the tile, so no wait for a copy sits inside a
+//    tile; the row max crosses the two 32-lane halves with V_PERMLANE32_SWAP.
 //  * workgroups are ordered head-major and handed to the 8 XCDs in contiguous
 //    ranges, so the workgroups sharing an XCD's L2 stream the same K/V blocks.
 #include <type_traits>
@@ -82,36 +85,28 @@ __device__ __forceinline__ float max_across_halves(float x) {
   return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
-// MFMA bursts run at raised wave priority, so a wavefront's MFMAs are issued
-// as soon as the matrix unit frees up while the SIMD's other wavefront runs VALU
-// work.
-__device__ __forceinline__ void mfma_phase_begin() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(1);
-  __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void mfma_phase_end() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(0);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
+// The kernel is software-pipelined inside every wavefront so that each MFMA
+// burst has independent VALU work beside it:
+//   stage 1 of tile t: the Q.K MFMAs of tile t, beside them the flush of tile
+//            t-1's P bytes (codes 1..7 -> 0) and the row max of tile t;
+//   stage 2 of tile t: the ExpCast bytes of tile t (one fmaf + one byte
+//            conversion per score), beside them the P.V and row-sum MFMAs of
+//            tile t-1.
+// V is copied one tile behind K (V of tile t during tile t, K of tile t+1
+// during tile t), so two buffers of each still suffice.  The accumulators see
+// the same sequence as in the unpipelined order: P.V of tile t-1 is added in
+// the scale of the running max after tile t-1, then the rescale to tile t's
+// max.  A tile's row sum is taken into l (times the rescale that followed it)
+// at the start of the next tile, and a batch of four row sums is restored in
+// the tile after that, so no wavefront waits for an MFMA result.
 template <int kPMode, bool kDump, int kVF>
 __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   constexpr bool kFP4 = kVF == VC_V_MXFP4;
-  // V tile bytes in global memory: E4M3 128 x 128; MXFP4 128 channels x 64
-  // bytes, then (in LDS only) the 512 bytes of E8M0 scales at offset 8192
   constexpr int kVTile = kFP4 ? kTile / 2 : kTile;
-  // The two buffers of each operand are separate LDS objects so that reads of
-  // one are not ordered behind the asynchronous copies into the other (the
-  // copies are tracked by the vector memory counter).
   __shared__ __align__(16) uint8_t Ks0[kTile];
   __shared__ __align__(16) uint8_t Ks1[kTile];
   __shared__ __align__(16) uint8_t Vs0[kTile];
   __shared__ __align__(16) uint8_t Vs1[kTile];
-  // A operands of the batched mean restore: per batch of four KV blocks, 16
-  // bytes per (channel block cb, lane half g, column col): bf16 [hi, lo, hi, 0]
-  // of mean_t / sv for channel 32 cb + col and blocks 2g, 2g + 1 of the batch.
   __shared__ __align__(16) uint32_t MuB[2][1024];
   __shared__ float InvSv[kD];
   __shared__ float Sv[kD];
@@ -120,9 +115,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   const int item = xcd_item(blockIdx.x, npair * a.BH);
   const int bh = item / npair, pr = item % npair;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
-  // wavefronts 4w..4w+3 take query block 2*pr + w; when nb is odd the last
-  // pair's second block does not exist: it repeats the first and stores nothing
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool qvalid = 2 * pr + (wave >> 2) < a.nb;
   const int qb = qvalid ? 2 * pr + (wave >> 2) : 2 * pr;
   const int g = lane >> 5, col = lane & 31;
@@ -131,12 +124,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
 
   if (tid < kD) {
     const float sv = a.vs[(long long)bh * kD + tid];
-    const float svp = sv > 0.0f ? sv : 1.0f;   // an all-zero residual channel keeps its mean
+    const float svp = sv > 0.0f ? sv : 1.0f;
     Sv[tid] = svp;
     InvSv[tid] = 1.0f / svp;
   }
-
-  // Q operand (B of S^T = K.Q^T): query row, 32 bytes per channel half.
   const int qrow = qb * kBlock + (wave & 3) * 32 + col;
   v8i qop[2];
   {
@@ -149,75 +140,40 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
       qop[c2][4] = hi.x; qop[c2][5] = hi.y; qop[c2][6] = hi.z; qop[c2][7] = hi.w;
     }
   }
-  // uniform: held in a scalar register, so no wait on it inside the tile loop
   const float sq = __builtin_bit_cast(
       float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.qs[(long long)bh * nb + qb])));
 
   const uint8_t* kbase = a.k + (long long)bh * Np * kD;
   const uint8_t* vbase = a.v + (long long)bh * nb * kVTile;
   const uint16_t* mbase = a.means + (long long)bh * nb * kD;
-
-  // K and V^T tiles go global -> LDS directly.  Instruction j (16 per tile,
-  // 4 per wave) fills LDS bytes [1024j, 1024j+1024): lane i writes row
-  // 8j + i/8 at chunk position i%8, so it fetches the global chunk that the
-  // XOR swizzle puts there.
-  // The copies go through buffer resources (one head's nb tiles each), so the
-  // tile offset is a scalar and a lane keeps only 32-bit in-tile offsets.
-  // Rows of instructions i and i+2 differ by 64, which leaves swz_k unchanged,
-  // and rows of any two differ by a multiple of 32, which leaves swz_v
-  // unchanged: three lane offsets plus scalar offsets cover all eight copies.
   uint32_t mr = 0;
-  float ksn = 0.0f;   // K scale of the block in flight; becomes the next block's
+  float ksn = 0.0f;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)nb * kTile);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)nb * kVTile);
-  // MXFP4 scales: 512 bytes per tile; lanes 32..63 of the copy read the next
-  // tile's (or, past the end, zeros) into unused LDS bytes
   const __amdgpu_buffer_rsrc_t vgrs = make_rsrc(kFP4 ? a.vg + (long long)bh * nb * 512 : a.v, (uint32_t)nb * 512);
-  uint32_t dkoff, dvoff;   // copy j = wave + 8i: rows of i = 0, 1 differ by 64 (neither swizzle changes)
+  uint32_t dkoff, dvoff;
   {
     const int pos = lane & 7;
     const int row = 8 * wave + (lane >> 3);
     dkoff = (uint32_t)(row * kD + 16 * (pos ^ swz_k(row)));
     dvoff = (uint32_t)(row * kD + 16 * (pos ^ swz_v(row)));
-    if (kFP4) {   // one copy per wavefront: channel rows 16 wave .. 16 wave + 15, 4 chunks of 16 bytes each
+    if (kFP4) {
       const int r4 = 16 * wave + (lane >> 2);
       dvoff = (uint32_t)(r4 * 64 + 16 * ((lane & 3) ^ ((r4 >> 2) & 3)));
     }
   }
-  auto load_tile = [&](int t, int buf) {
-    const uint32_t toff = (uint32_t)t * kTile;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = wave + 8 * i;
-      dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * j, dkoff, toff + 8192u * i);
-      if (!kFP4) dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * j, dvoff, toff + 8192u * i);
-    }
-    if (kFP4) {
-      dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * wave, dvoff, (uint32_t)t * kVTile);
-      if (wave == 0) dma16_buf(vgrs, (buf ? Vs1 : Vs0) + 8192, (uint32_t)lane * 16u, (uint32_t)t * 512u);
-    }
-    if (tid < kD) mr = mbase[(long long)t * kD + tid];
-    ksn = a.ks[(long long)bh * nb + t];   // K scale of the block being copied
+  // half i (0, 1) of K tile t into buffer buf
+  auto copy_k = [&](int t, int buf, int i) {
+    dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * (wave + 8 * i), dkoff, (uint32_t)t * kTile + 8192u * i);
   };
-  // copy p (0..3) of tile t: E4M3 K half 0, V half 0, K half 1, V half 1;
-  // MXFP4 K half 0, K half 1, V, E8M0 scales (wavefront 0).  Past the last tile
-  // the buffer resources read zeros into a buffer that is not read again.
-  auto copy_piece = [&](int t, int buf, int p) {
-    const uint32_t toff = (uint32_t)t * kTile;
-    if (!kFP4) {
-      const int i = p >> 1, j = wave + 8 * i;
-      if ((p & 1) == 0) dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * j, dkoff, toff + 8192u * i);
-      else dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * j, dvoff, toff + 8192u * i);
-    } else if (p < 2) {
-      dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * (wave + 8 * p), dkoff, toff + 8192u * p);
-    } else if (p == 2) {
-      dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * wave, dvoff, (uint32_t)t * kVTile);
-    } else if (wave == 0) {
-      dma16_buf(vgrs, (buf ? Vs1 : Vs0) + 8192, (uint32_t)lane * 16u, (uint32_t)t * 512u);
-    }
+  // piece i (0, 1) of V tile t into buffer buf: E4M3 the two halves; MXFP4 the
+  // codes, then the E8M0 scales (wavefront 0).  Past the last tile the buffer
+  // resources read zeros into a buffer that is not read again.
+  auto copy_v = [&](int t, int buf, int i) {
+    if (!kFP4) dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * (wave + 8 * i), dvoff, (uint32_t)t * kTile + 8192u * i);
+    else if (i == 0) dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * wave, dvoff, (uint32_t)t * kVTile);
+    else if (wave == 0) dma16_buf(vgrs, (buf ? Vs1 : Vs0) + 8192, (uint32_t)lane * 16u, (uint32_t)t * 512u);
   };
-  // mean_t / sv of tile t as a bf16 pair: hi = the value truncated to bf16
-  // (exact difference), lo = the remainder rounded to bf16
   auto store_means = [&](int t) {
     if (tid < kD) {
       const float mu = bf16_bits_to_f32(mr) * InvSv[tid];
@@ -232,11 +188,17 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     }
   };
 
-  load_tile(0, 0);
+  copy_k(0, 0, 0);
+  copy_k(0, 0, 1);
+  if (tid < kD) mr = mbase[tid];
+  ksn = a.ks[(long long)bh * nb];
   float ksc = ksn;
-  // slots of blocks past the last one stay zero (0 x 0 in the final batch)
   reinterpret_cast<uint4*>(&MuB[0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);
-  __syncthreads();          // InvSv ready
+  // V buffer 1 holds no tile before tile 1's copy: zeros, so that the (all-zero)
+  // P.V of "tile -1" in the first step reads finite values
+  reinterpret_cast<uint4*>(Vs1)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4*>(Vs1)[tid + kAttnThreads] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
   store_means(0);
   wait_dma();
   __syncthreads();
@@ -248,32 +210,19 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
   float mx = -__builtin_inff();
   float l = 0.0f;
-  // Row sums come from V_MFMA_F32_16X16X128_F8F6F4 with a P half (64 keys) as
-  // the B operand: B lane l is column l%16 of k-group l/16, which holds query
-  // l%32 over 32 of the half's keys.  A lane l (row l%16, k-group l/16) is E4M3
-  // 1.0 when bit 2 of the row equals the parity of the k-group and 0 otherwise,
-  // so output row r sums the two k-groups of query (r%8 < 4 ? col : col + 16).
-  // Output lane l holds rows 4(l/16)..4(l/16)+3 of column l%16, which is the
-  // row sum of query l%32: the lane's own query.
   v8i ones;
   {
     const int on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) ones[i] = on ? 0x38383838 : 0;
   }
-  // The mean restore is batched over four KV blocks: rsb[s] holds the row sum
-  // of block s of the batch (rescaled with the accumulators while pending), and
-  // one bf16 V_MFMA_F32_32X32X16_BF16 per 32-channel block adds
-  // sum_s rsb[s] * mean_s / sv with each factor split into a bf16 pair
-  // (hi*hi + lo*hi + hi*lo, three of the 16 k-slots per block; the dropped
-  // lo*lo term and the rounding of lo are below 2^-16 of the product).
   float rsb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  // The row sum of tile t is taken into l and rsb at the start of tile t + 1
-  // (before that tile's rescale, so the arithmetic is unchanged): nothing waits
-  // for the P.V MFMAs at the end of a tile, and they drain during the barrier.
-  float rsp = 0.0f;
-  // U += sum_s rsb[s] (x) mean_s / sv for the batch held in MuB[mbuf]: lanes of
-  // half g carry blocks 2g, 2g + 1 as B k-slots [hi, hi, lo, 0] of each row sum
+  v4f rsacc = {0.0f, 0.0f, 0.0f, 0.0f};   // row sum of the tile whose P.V ran last (pending)
+  float alpha_prev = 1.0f;                 // rescale applied after that P.V
+  uint32_t pk[16];                         // P bytes of the previous tile (pending flush and P.V)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pk[i] = 0u;
+
   auto restore = [&](int mbuf) {
     const float x0 = g ? rsb[2] : rsb[0];
     const float x1 = g ? rsb[3] : rsb[1];
@@ -289,21 +238,23 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rsb[i] = 0.0f;
   };
-  // LDS operand addresses: the K rows sigma(m, col) of the four 32-key blocks
-  // differ by multiples of 16 rows and the V rows 32*cb + col by multiples of 32,
-  // neither of which changes the swizzle, so four base offsets per operand plus
-  // compile-time offsets cover every read.
+  // the pending row sum (times the rescale after it) joins l and slot sl of the batch
+  auto take_rowsum = [&](int sl) {
+    const float rv = rsacc[0] * alpha_prev;
+    l += rv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rsb[i] = i == sl ? rv : rsb[i];
+  };
   uint32_t lk[4], lv[4];
   {
     const int kr = sigma(0, col), ksw = swz_k(kr), vsw = swz_v(col);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = 4 * (i >> 1) + 2 * g + (i & 1);    // chunks 2g, 2g+1, 4+2g, 5+2g
+      const int c = 4 * (i >> 1) + 2 * g + (i & 1);
       lk[i] = (uint32_t)(kr * kD + 16 * (c ^ ksw));
       lv[i] = (uint32_t)(col * kD + 16 * (c ^ vsw));
     }
   }
-  // MXFP4 V^T operand: channel row 32cb + col, chunk 2h + g, swizzled like the copy
   uint32_t lv4[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) lv4[h] = (uint32_t)(col * 64 + 16 * ((2 * h + g) ^ ((col >> 2) & 3)));
@@ -314,125 +265,32 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
     return r;
   };
-
-  // one KV block; the LDS buffer index is a compile-time constant so every
-  // LDS address is a base register plus an immediate offset
-  auto step = [&](const int t, auto slotc) {
-    constexpr int slot = decltype(slotc)::value;   // t % 4: block within the restore batch
-    constexpr int buf = slot & 1;
-    if (t + 1 < nb) {
-      if (tid < kD) mr = mbase[(long long)(t + 1) * kD + tid];
-      ksn = a.ks[(long long)bh * nb + t + 1];   // K scale of the block being copied
+  // flush codes 1..7 of the pending P bytes to 0, eight bytes at a time: codes
+  // are <= 56, so adding 0x78 to every byte carries nowhere and sets a byte's
+  // top bit exactly when its code is >= 8; V_PERM_B32 spreads those top bits
+  // (bytes 1, 3 directly, bytes 0, 2 from the copy shifted left by 8) into byte masks
+  auto flush = [&]() {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint64_t w64 = ((uint64_t)pk[2 * q + 1] << 32) | pk[2 * q];
+      const uint64_t t = w64 + 0x7878787878787878ull;
+      const uint64_t t8 = t << 8;
+      pk[2 * q] &= __builtin_amdgcn_perm((uint32_t)t8, (uint32_t)t, 0x090B080Au);
+      pk[2 * q + 1] &= __builtin_amdgcn_perm((uint32_t)(t8 >> 32), (uint32_t)(t >> 32), 0x090B080Au);
     }
-
-    // ---- row sum of the previous tile; restore of the batch it completed ----
-    if (slot != 0 || t > 0) {
-      l += rsp;
-      rsb[(slot + 3) & 3] = rsp;
-    }
-    // ---- S^T = K_t . Q^T : 4 blocks of 32 keys x 32 queries ----
-    mfma_phase_begin();
-    if (slot == 0 && t > 0) restore(((t >> 2) - 1) & 1);
-    v16f s[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[m][r] = 0.0f;
-      const uint8_t* kb = (buf ? Ks1 : Ks0) + kD * (64 * (m >> 1) + 16 * (m & 1));
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-        s[m] = mfma32(op8(ld16(kb + lk[2 * c2]), ld16(kb + lk[2 * c2 + 1])), qop[c2], s[m]);
-      // the next tile's copies, one per pair of Q.K MFMAs, so that they drain
-      // through the address unit while the MFMAs run
-      copy_piece(t + 1, buf ^ 1, m);
-    }
-    mfma_phase_end();
-    // keys beyond N (last tile only) take no part
-    if ((t + 1) * kBlock > N) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 64 * (m >> 1) + 32 * g + 16 * (m & 1) + r;
-          if (t * kBlock + key >= N) s[m][r] = -__builtin_inff();
-        }
-    }
-    // ---- running max (log2 units) ----
-    float M = s[0][0];
+  };
+  // keys at or beyond N of tile t (the last): P byte 0 whatever the score scale
+  auto mask_pk = [&](int t) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) M = fmaxf(M, s[m][r]);
-    M = max_across_halves(M);
-    const float kap = (sq * ksc) * a.c0;
-    const float mx_new = fmaxf(mx, M * kap);
-
-    // ---- P bytes, laid out as the B operand of the P.V MFMA ----
-    uint32_t pk[16];
-    if (kPMode == VC_P_EXPCAST) {
-      const float A = 8.0f * kap;
-      const float Bc = 55.65f - 8.0f * mx_new;
-      // codes never exceed 56 unless rounding of a huge running max pushes the
-      // row maximum past 56.5; then clamp (the oracle clamps at 56 as well)
-      if (__builtin_expect(__any(__builtin_fmaf(M, A, Bc) >= 56.5f), 0)) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[m][r] = fminf(s[m][r], (56.0f - Bc) / A);
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int key0 = t * kBlock + 64 * (m >> 1) + 32 * g + 16 * (m & 1) + 4 * r4;
+        const int nv = min(max(N - key0, 0), 4);
+        pk[4 * m + r4] &= nv >= 4 ? 0xFFFFFFFFu : (1u << (8 * nv)) - 1u;
       }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          uint32_t w = 0u;
-#pragma unroll
-          for (int b = 0; b < 4; ++b)   // round to nearest even, clamp to [0,255], pack
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[m][4 * r4 + b], A, Bc), b, w);
-          wv[r4] = w;
-        }
-        // flush codes 1..7 (below the E4M3 normal range) to 0, eight bytes at a
-        // time: codes are <= 56, so adding 0x78 to every byte carries nowhere and
-        // sets a byte's top bit exactly when its code is >= 8; V_PERM_B32 spreads
-        // those top bits (bytes 1, 3 directly, bytes 0, 2 from the copy shifted
-        // left by 8) into byte masks.
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const uint64_t w64 = ((uint64_t)wv[2 * pr + 1] << 32) | wv[2 * pr];
-          const uint64_t t = w64 + 0x7878787878787878ull;
-          const uint64_t t8 = t << 8;
-          pk[4 * m + 2 * pr] = wv[2 * pr] & __builtin_amdgcn_perm((uint32_t)t8, (uint32_t)t, 0x090B080Au);
-          pk[4 * m + 2 * pr + 1] =
-              wv[2 * pr + 1] & __builtin_amdgcn_perm((uint32_t)(t8 >> 32), (uint32_t)(t >> 32), 0x090B080Au);
-        }
-      }
-    } else {   // VC_P_FP32EXP_E4M3: conventional exp2 then E4M3 conversion
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          float p[4];
-#pragma unroll
-          for (int b = 0; b < 4; ++b) p[b] = __builtin_amdgcn_exp2f(s[m][4 * r4 + b] * kap - mx_new);
-          pk[4 * m + r4] = __builtin_amdgcn_cvt_pk_fp8_f32(
-              p[2], p[3], __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0u, false), true);
-        }
-    }
-
-    // keys at or beyond N (last tile only): P byte 0.  Their scores were set
-    // to -inf for the row max, and -inf * kap is NaN when kap = 0 (an all-zero
-    // Q block or K block has scale 0), so the bytes are cleared after the fact.
-    if ((t + 1) * kBlock > N) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int key0 = t * kBlock + 64 * (m >> 1) + 32 * g + 16 * (m & 1) + 4 * r4;
-          const int nv = min(max(N - key0, 0), 4);   // valid keys among the four bytes
-          pk[4 * m + r4] &= nv >= 4 ? 0xFFFFFFFFu : (1u << (8 * nv)) - 1u;
-        }
-    }
-
+  };
+  auto dump_p = [&](int t) {
     if (kDump && qvalid && qrow < N) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -440,27 +298,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int key = 64 * (m >> 1) + 32 * g + 16 * (m & 1) + r;
           const long long idx = ((long long)bh * N + qrow) * Np + (long long)t * kBlock + key;
-          const bool valid = t * kBlock + key < N;
-          a.sdump[idx] = valid ? s[m][r] : 0.0f;
-          a.pdump[idx] = (uint8_t)(valid ? (pk[4 * m + (r >> 2)] >> (8 * (r & 3))) & 0xFFu : 0u);
+          a.pdump[idx] = (uint8_t)(t * kBlock + key < N ? (pk[4 * m + (r >> 2)] >> (8 * (r & 3))) & 0xFFu : 0u);
         }
     }
-
-    // ---- rescale the accumulators when the running max moved ----
-    const float alpha = __builtin_amdgcn_exp2f(mx - mx_new);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
-#pragma unroll
-      for (int i = 0; i < slot; ++i) rsb[i] *= alpha;
-    }
-    l *= alpha;
-    mx = mx_new;
-
-    // ---- O^T += V^T_t . P^T ; row sums from an all-ones operand ----
-    mfma_phase_begin();
+  };
+  // O^T += V^T . P^T for the pending P bytes (V tile in buffer vb), and their row sums
+  auto pv = [&](auto vbc) {
+    constexpr int vbuf = decltype(vbc)::value;
     v4f rs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -470,19 +314,173 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         if constexpr (kFP4) {
-          const uint8_t* vb = (buf ? Vs1 : Vs0) + 64 * 32 * cb;
-          const int sc = (int)*reinterpret_cast<const uint16_t*>((buf ? Vs1 : Vs0) + 8192 + (32 * cb + col) * 4 + 2 * g);
+          const uint8_t* vb = (vbuf ? Vs1 : Vs0) + 64 * 32 * cb;
+          const int sc = (int)*reinterpret_cast<const uint16_t*>((vbuf ? Vs1 : Vs0) + 8192 + (32 * cb + col) * 4 + 2 * g);
           o[cb] = h == 0 ? mfma_pv_fp4<0>(ld16(vb + lv4[0]), pop, sc, o[cb])
                          : mfma_pv_fp4<1>(ld16(vb + lv4[1]), pop, sc, o[cb]);
         } else {
-          const uint8_t* vb = (buf ? Vs1 : Vs0) + kD * 32 * cb;
+          const uint8_t* vb = (vbuf ? Vs1 : Vs0) + kD * 32 * cb;
           o[cb] = mfma32(op8(ld16(vb + lv[2 * h]), ld16(vb + lv[2 * h + 1])), pop, o[cb]);
         }
       }
       rs = mfma16(ones, pop, rs);
     }
-    rsp = rs[0];   // taken into l and rsb at the start of the next tile
-    mfma_phase_end();
+    rsacc = rs;
+  };
+
+  // one KV tile (slot = t % 4, compile-time).  The MFMA bursts and the VALU
+  // work beside them share one basic block: in the first steps the pending
+  // row sum, P bytes and restore batch are zeros, so no step branches on t.
+  auto step = [&](const int t, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+    constexpr int cur = slot & 1;   // buffers of K tile t and V tile t; V tile t-1 is in cur ^ 1
+    {
+      const int tn = min(t + 1, nb - 1);   // next block (the last step reloads its own, unused)
+      if (tid < kD) mr = mbase[(long long)tn * kD + tid];
+      ksn = a.ks[(long long)bh * nb + tn];
+    }
+    // ---- the row sum of tile t-2 joins l ----
+    take_rowsum((slot + 2) & 3);
+
+    // ---- stage 1: S^T = K_t . Q^T; beside it the flush of tile t-1's P bytes ----
+    __builtin_amdgcn_sched_barrier(0);
+    v16f s[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[m][r] = 0.0f;
+      const uint8_t* kb = (cur ? Ks1 : Ks0) + kD * (64 * (m >> 1) + 16 * (m & 1));
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+        s[m] = mfma32(op8(ld16(kb + lk[2 * c2]), ld16(kb + lk[2 * c2 + 1])), qop[c2], s[m]);
+      if ((m & 1) == 0) copy_k(t + 1, cur ^ 1, m >> 1);
+      else copy_v(t, cur, m >> 1);
+    }
+    if (kPMode == VC_P_EXPCAST) flush();
+    // the flushed bytes are materialised here, inside the Q.K region (the
+    // optimiser would otherwise sink the flush next to its use in stage 2)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(pk[i]));
+    // row max of the 32-key blocks, each once its two MFMAs are done (keys
+    // past N are taken out below, on the last tile only)
+    float Mb[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      Mb[m] = s[m][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) Mb[m] = fmaxf(Mb[m], s[m][r]);
+    }
+    // issue order: the operand reads run two MFMAs ahead, so their latency
+    // passes under the VALU work (the flush, and the block maxima as their
+    // scores arrive) that follows each MFMA; a tile copy after every second MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // LDS reads of MFMAs 0, 1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA i
+      __builtin_amdgcn_sched_group_barrier(0x002, kPMode == VC_P_EXPCAST ? 8 : 3, 0);   // VALU
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads of MFMA i + 2
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // tile copy
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float M = fmaxf(fmaxf(Mb[0], Mb[1]), fmaxf(Mb[2], Mb[3]));
+    if ((t + 1) * kBlock > N) {   // last tile: keys beyond N take no part
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 64 * (m >> 1) + 32 * g + 16 * (m & 1) + r;
+          if (t * kBlock + key >= N) s[m][r] = -__builtin_inff();
+        }
+      M = s[0][0];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) M = fmaxf(M, s[m][r]);
+    }
+    if (t > 0) dump_p(t - 1);
+    if (kDump && qvalid && qrow < N) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 64 * (m >> 1) + 32 * g + 16 * (m & 1) + r;
+          const long long idx = ((long long)bh * N + qrow) * Np + (long long)t * kBlock + key;
+          a.sdump[idx] = t * kBlock + key < N ? s[m][r] : 0.0f;
+        }
+    }
+    M = max_across_halves(M);
+    const float kap = (sq * ksc) * a.c0;
+    const float mx_new = fmaxf(mx, M * kap);
+
+    // ---- the rescale to tile t-1's max, deferred from the previous step so that
+    // it never waits for the P.V MFMAs just issued; then a completed batch of
+    // four row sums is restored (accumulators and row sums in the same scale) ----
+    if (__any(alpha_prev != 1.0f)) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[cb][r] *= alpha_prev;
+    }
+    if (slot == 1) restore(((t - 2) >> 2) & 1);
+
+    // ---- stage 2: P bytes of tile t; beside them P.V and row sums of tile t-1 ----
+    uint32_t pn[16];
+    __builtin_amdgcn_sched_barrier(0);
+    if (kPMode == VC_P_EXPCAST) {
+      const float A = 8.0f * kap;
+      const float Bc = 55.65f - 8.0f * mx_new;
+      if (__builtin_expect(__any(__builtin_fmaf(M, A, Bc) >= 56.5f), 0)) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[m][r] = fminf(s[m][r], (56.0f - Bc) / A);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          uint32_t w = 0u;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(s[m][4 * r4 + b], A, Bc), b, w);
+          pn[4 * m + r4] = w;
+        }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float p[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) p[b] = __builtin_amdgcn_exp2f(s[m][4 * r4 + b] * kap - mx_new);
+          pn[4 * m + r4] = __builtin_amdgcn_cvt_pk_fp8_f32(
+              p[2], p[3], __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0u, false), true);
+        }
+    }
+    pv(std::integral_constant<int, cur ^ 1>{});
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(pn[i]));
+    // issue order: operand reads two P.V MFMAs ahead; after each of the ten
+    // MFMAs (eight P.V, two row sums) a share of the P bytes of tile t
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kPMode == VC_P_EXPCAST ? 13 : 22, 0);
+      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- rescale to tile t's max: l and the pending row sums now, the
+    // accumulators (which tile t-1's P.V MFMAs are still writing) next step ----
+    const float alpha = __builtin_amdgcn_exp2f(mx - mx_new);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rsb[i] *= alpha;
+    l *= alpha;
+    alpha_prev = alpha;
+    mx = mx_new;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pk[i] = pn[i];
 
     if (t + 1 < nb) store_means(t + 1);
     wait_dma();
@@ -496,16 +494,24 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     if (t + 2 < nb) step(t + 2, std::integral_constant<int, 2>{});
     if (t + 3 < nb) step(t + 3, std::integral_constant<int, 3>{});
   }
-  // the last tile's row sum and the restore of the final (possibly partial) batch
-  l += rsp;
-  {
-    const int sl = (nb - 1) & 3;
+  // ---- drain: row sum of tile nb-2, P.V and row sum of tile nb-1, last restores ----
+  if (nb >= 2) take_rowsum((nb - 2) & 3);
+  if (__any(alpha_prev != 1.0f)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rsb[i] = i == sl ? rsp : rsb[i];
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[cb][r] *= alpha_prev;
   }
+  if (nb >= 2 && ((nb - 2) & 3) == 3) restore(((nb - 2) >> 2) & 1);
+  if (kPMode == VC_P_EXPCAST) flush();
+  mask_pk(nb - 1);
+  dump_p(nb - 1);
+  if ((nb - 1) & 1) pv(std::integral_constant<int, 1>{});
+  else pv(std::integral_constant<int, 0>{});
+  alpha_prev = 1.0f;
+  take_rowsum((nb - 1) & 3);
   restore(((nb - 1) >> 2) & 1);
 
-  // ---- epilogue: O = sv * U / l, original query order ----
   if (qvalid && qrow < N) {
     const float invl = 1.0f / l;
     float* op = a.out + ((long long)bh * N + qrow) * kD;
