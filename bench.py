@@ -50,10 +50,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--kernel-reps", type=int, default=10)
-    ap.add_argument("--profile", choices=("attn", "group", "copy", "mxfp4"), default=None,
+    ap.add_argument("--profile", choices=("attn", "group", "copy", "mxfp4", "ablation"), default=None,
                     help="short run for a profiler: attention kernel only, grouping + preprocessing "
-                         "(Q skipped), a plain 1 GiB device copy (counter calibration), or the MXFP4 "
-                         "(4-bit V residual) attention with both FP8 P paths")
+                         "(Q skipped), a plain 1 GiB device copy (counter calibration), the MXFP4 "
+                         "(4-bit V residual) attention with both FP8 P paths, or the E4M3 attention with "
+                         "both P paths on the ExpCast-ablation workload (B1 H8 N8192) and the Wan2.2 shape")
     return ap.parse_args()
 
 
@@ -101,6 +102,93 @@ def fidelity(Qd, Kd, Vd, out, scale, rows_per_head=64):
     return math.sqrt(num / den), f"{rows_per_head} evenly spaced query rows of each of {B * H} heads"
 
 
+class ClockSampler:
+    """Samples the GPU shader clock from sysfs (the '*' level of pp_dpm_sclk)
+    every 20 ms in a thread while the timed work runs; mean MHz or None when the
+    file is not readable on this machine."""
+
+    def __init__(self):
+        import glob
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self._stop = None
+
+    def _read(self):
+        import re
+        for pth in self.paths:
+            try:
+                with open(pth) as fh:
+                    for line in fh:
+                        if line.rstrip().endswith("*"):
+                            m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                            if m:
+                                return int(m.group(1))
+            except OSError:
+                continue
+        return None
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+                self._stop.wait(0.02)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def mean(self):
+        return round(sum(self.samples) / len(self.samples), 1) if self.samples else None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def p_path_ablation(vc, W, reps, stream, workloads=("expcast-ablation", "wan22-attention"), preps=None):
+    """Attention time of the E4M3 kernel with each P path (ExpCast and fp32 exp2 +
+    E4M3 conversion) on one cached permutation per workload."""
+    import torch
+    res = {}
+    for name in workloads:
+        c = W.WORKLOADS[name]
+        if preps is not None and name in preps:
+            prep = preps[name]
+        else:
+            Q, K, V = W.make_inputs(name)
+            dev = torch.device("cuda:0")
+            Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+            perm, _, _ = vc.vsmooth_group(Vd, c["k"], c["iters"])
+            prep = vc.preprocess_quant(Qd, Kd, Vd, perm)
+        B, H, N = prep["B"], prep["H"], prep["N"]
+        out = torch.empty(B, H, N, 128, dtype=torch.float32, device=prep["k_codes"].device)
+        flops = 4.0 * N * N * 128 * H * B
+        row = {"shape": f"B{B} H{H} N{N}"}
+        for pm in ("expcast", "fp32exp_e4m3"):
+            vc.attn_fp8_fwd(prep, 1.0 / math.sqrt(128.0), pm, out=out)
+            ms = timed(lambda: vc.attn_fp8_fwd(prep, 1.0 / math.sqrt(128.0), pm, out=out), reps, stream)
+            row[pm] = {"ms": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        row["expcast_speedup"] = round(row["fp32exp_e4m3"]["ms"] / row["expcast"]["ms"], 3)
+        res[name] = row
+    return res
+
+
 def timed(fn, reps, stream):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -145,6 +233,7 @@ def cpu_baseline(Q, K, V, c, scale):
         "value": flops / total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"head 0 of {H}: k-means+sort {t1 - t0:.2f}s, preprocess {t2 - t1:.2f}s, "
                    f"attention of {len(rows)} of {N} query rows {t3 - t2:.2f}s; "
@@ -197,6 +286,10 @@ def main():
             print(f"[bench] MXFP4 attention, {pm} x{args.kernel_reps}: {ms_attn:.3f} ms per call", file=sys.stderr,
                   flush=True)
         return
+    if args.profile == "ablation":
+        res = p_path_ablation(vc, W, 2, stream)
+        print(f"[bench] P-path ablation x2: {json.dumps(res)}", file=sys.stderr, flush=True)
+        return
     if args.profile == "attn":
         perm, _, _ = vc.vsmooth_group(Vd, c["k"], c["iters"])
         prep = vc.preprocess_quant(Qd, Kd, Vd, perm)
@@ -227,8 +320,11 @@ def main():
     perm = state["perm"]
     ms_group = timed(lambda: vc.vsmooth_group(Vd, c["k"], c["iters"]), 3, stream)
     ms_prep = timed(lambda: vc.preprocess_quant(Qd, Kd, Vd, perm), 5, stream)
-    ms_attn = timed(lambda: vc.attn_fp8_fwd(prep, scale, "expcast", out=out), args.kernel_reps, stream)
+    with ClockSampler() as clk:
+        ms_attn = timed(lambda: vc.attn_fp8_fwd(prep, scale, "expcast", out=out), args.kernel_reps, stream)
     ms_bf16 = timed(lambda: vc.attn_bf16_fwd(Qd, Kd, Vd, scale, out=out), 3, stream)
+    ablation = p_path_ablation(vc, W, 5, stream, preps={WORKLOAD: prep})
+    print(f"[bench] P-path ablation: {json.dumps(ablation)}", file=sys.stderr, flush=True)
     print(f"[bench] group {ms_group:.2f} ms, preprocess {ms_prep:.2f} ms, attention {ms_attn:.2f} ms, "
           f"bf16 comparator {ms_bf16:.2f} ms", file=sys.stderr, flush=True)
 
@@ -266,6 +362,8 @@ def main():
         "stages_ms": {"vsmooth_group": round(ms_group, 3), "preprocess_quant": round(ms_prep, 3),
                       "attn_fp8_expcast": round(ms_attn, 3)},
         "attn_kernel_tflops": round(achieved, 1),
+        "sclk_mhz_during_attention": clk.mean(),
+        "p_path_ablation": ablation,
         "bf16_comparator": {"ms": round(ms_bf16, 3), "tflops": round(flops / (ms_bf16 * 1e-3) / 1e12, 1),
                             "speedup_of_fp8_kernel": round(ms_bf16 / ms_attn, 3)},
         "fidelity_rel_l2_vs_exact_fp32": {"attn_fp8_expcast": float(f"{fid_fp8:.4e}"),

@@ -482,7 +482,7 @@ def score_scale(softmax_scale: float) -> np.float32:
     return F32(np.float64(F32(softmax_scale)) * LOG2E)
 
 
-def expcast_codes(S: np.ndarray, kap: np.ndarray, mx: np.ndarray) -> np.ndarray:
+def expcast_codes(S: np.ndarray, kap: np.ndarray, mx: np.ndarray, octave_offset: int = 0) -> np.ndarray:
     """ExpCast-FP8: the E4M3 byte of p = 2^(S*kap - mx) written straight from
     the log-domain score.
 
@@ -494,13 +494,18 @@ def expcast_codes(S: np.ndarray, kap: np.ndarray, mx: np.ndarray) -> np.ndarray:
     Exact reading: A = 8*kap, Bc = float32(55.65 - 8*mx),
     code = RNE(fmaf(S, A, Bc)); codes below 8 (under the normal range) -> 0x00;
     codes above 56 cannot occur and are clamped as a guard.
-    S: float32 [R, T]; kap, mx: float32 [R]."""
+    S: float32 [R, T]; kap, mx: float32 [R].
+    octave_offset (a fidelity diagnostic only, never the method's default):
+    P pre-scaled by 2^octave_offset, i.e. 8*octave_offset added to the
+    constant; the row maximum then maps to code 56 + 8*octave_offset (at most
+    8 octaves keeps every code finite), so fewer small probabilities fall below
+    the normal range; the normalisation cancels the scale."""
     kap = f32(kap)
     A = f32(F32(8.0) * kap)
-    Bc = f32(EXPCAST_OFFSET - f32(F32(8.0) * f32(mx)))
+    Bc = f32(f32(EXPCAST_OFFSET + F32(8 * octave_offset)) - f32(F32(8.0) * f32(mx)))
     code_f = fma_f32(S, A[:, None], Bc[:, None])
     c = np.rint(code_f.astype(np.float64))
-    c = np.where(c < 8, 0, np.minimum(c, 56))
+    c = np.where(c < 8, 0, np.minimum(c, 56 + 8 * octave_offset))
     return c.astype(np.uint8)
 
 
@@ -518,7 +523,7 @@ def exp2_probs_f32(S: np.ndarray, kap: np.ndarray, mx: np.ndarray) -> np.ndarray
 # ---------------------------------------------------------------------------
 
 def online_attention(Qd, Kd, Vres, means, N, qscale_rows, kscales, c0, p_mode, rows,
-                     record=None, scores=None):
+                     record=None, scores=None, octave_offset=0):
     """Blockwise non-causal attention with online softmax and block-mean restore.
 
     For each KV block t in permuted order (the order matters: P codes depend on
@@ -563,7 +568,7 @@ def online_attention(Qd, Kd, Vres, means, N, qscale_rows, kscales, c0, p_mode, r
             mx_new = np.maximum(mx, xmax.astype(np.float64))
             m32 = mx_new.astype(np.float32)
             if p_mode == "expcast":
-                codes = expcast_codes(S, kap, m32)
+                codes = expcast_codes(S, kap, m32, octave_offset)
                 P = e4m3_decode(codes)
             elif p_mode == "fp32exp_e4m3":
                 codes = e4m3_encode(exp2_probs_f32(S, kap, m32))
@@ -584,10 +589,12 @@ def online_attention(Qd, Kd, Vres, means, N, qscale_rows, kscales, c0, p_mode, r
     return U / l[:, None]
 
 
-def vc_attention_head(prep: dict, softmax_scale: float, p_mode: str, rows=None, record=None, scores=None):
+def vc_attention_head(prep: dict, softmax_scale: float, p_mode: str, rows=None, record=None, scores=None,
+                      octave_offset: int = 0):
     """VC attention output (float64 [rows, d], original query order) for one
     (batch, head) from the preprocessed codes of preprocess_head().  `scores`
-    optionally replaces the exact Q.K^T (see online_attention)."""
+    optionally replaces the exact Q.K^T (see online_attention); octave_offset
+    is the ExpCast fidelity diagnostic of expcast_codes (0 = the method)."""
     N = prep["N"]
     if rows is None:
         rows = np.arange(N)
@@ -597,7 +604,7 @@ def vc_attention_head(prep: dict, softmax_scale: float, p_mode: str, rows=None, 
     means = bf16_to_f32(prep["means"]).astype(np.float64)
     sq = prep["q_scales"][rows // BLOCK]
     return online_attention(Qd, Kd, prep["v_res"], means, N, sq, prep["k_scales"],
-                            score_scale(softmax_scale), p_mode, rows, record, scores)
+                            score_scale(softmax_scale), p_mode, rows, record, scores, octave_offset)
 
 
 def expcast_given_scores(S_tiles, kap_tiles, N):
