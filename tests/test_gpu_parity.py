@@ -334,14 +334,34 @@ def test_grouping_large_values(vc):
 
 
 def test_bf16_comparator_matches_exact_attention(vc):
+    """The comparator's only rounding of note is P -> bf16: each weight moves by
+    at most 2^-9 relative (the row sum is taken of the rounded weights, so the
+    normalisation follows), and the output of row i moves by at most
+    2^-9 / (1 - 2^-9) * sum_j w_ij |v_j - o_i| <= 2^-9 (1 + 2^-8) (sum_j w_ij |v_j| + |o_i|)
+    in L2 norm (w = exact softmax weights).  The bf16 products of the two MFMAs
+    are exact in fp32; the fp32 accumulation, the scaling of S and exp2 add
+    relative errors of order 2^-20, covered by a slack of 1e-5.  Each row is held
+    to that bound.  On these inputs the bf16 rounding of exact P alone (float64
+    otherwise) gives rel-L2 8.6e-4 and 9.0e-4 for the two heads, so the whole
+    output is held to 1.5e-3."""
     _say("bf16 comparator: B1 H2 N1000 against exact fp64 attention")
     Q, K, V = W.custom_inputs(1, 2, 1000, seed=11, recipe="clustered")
     dev = torch.device("cuda:0")
     out = vc.attn_bf16_fwd(Q.to(dev), K.to(dev), V.to(dev), SCALE).cpu().numpy()
     for h in range(2):
-        ex = O.exact_attention(_u16(Q[0, h]), _u16(K[0, h]), _u16(V[0, h]), SCALE)
-        # P is rounded to bf16 (relative error <= 2^-9 per element)
-        assert O.rel_l2(out[0, h], ex) < 4e-3
+        q16, k16, v16 = _u16(Q[0, h]), _u16(K[0, h]), _u16(V[0, h])
+        ex = O.exact_attention(q16, k16, v16, SCALE)
+        q, k, v = (O.bf16_to_f32(t).astype(np.float64) for t in (q16, k16, v16))
+        s = (q @ k.T) * SCALE
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        w /= w.sum(axis=1, keepdims=True)
+        wv = w @ np.linalg.norm(v, axis=1)
+        bound = 2.0 ** -9 * (1 + 2.0 ** -8) * (wv + np.linalg.norm(ex, axis=1)) + 1e-5 * wv
+        err = np.linalg.norm(out[0, h].astype(np.float64) - ex, axis=1)
+        assert np.all(err <= bound), f"h{h}: worst row {np.max(err / bound):.3f} of its bound"
+        rel = O.rel_l2(out[0, h], ex)
+        _say(f"bf16 comparator h{h}: rel-L2 {rel:.3e}, worst row at {np.max(err / bound):.3f} of its bound")
+        assert rel < 1.5e-3
 
 
 def test_wan22_full_size_sampled(vc):
