@@ -106,38 +106,44 @@ __global__ void __launch_bounds__(64) pre_pass1(const uint16_t* __restrict__ V, 
   }
 }
 
+// Half of a bf16 row (channels 64p .. 64p + 63) as 32 packed words (zero when
+// the row is past the block's end).
+__device__ __forceinline__ void load_half_row(const uint16_t* __restrict__ src, int row, bool valid, int p,
+                                              uint32_t (&w)[32]) {
+  if (valid) {
+    const uint4* rp = reinterpret_cast<const uint4*>(src + (long long)row * kD + 64 * p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 u = rp[j];
+      w[4 * j] = u.x; w[4 * j + 1] = u.y; w[4 * j + 2] = u.z; w[4 * j + 3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i] = 0u;
+  }
+}
+
 // Q or K rows (optionally) through RoPE and the Walsh-Hadamard transform, then
 // per-block E4M3 with scale = amax/448, all in registers: thread 2r + p holds channels 64p .. 64p + 63 of row r
-// (256 threads, 128 rows).  Arithmetic in fp32, in the order of the method's
+// (256 threads, 128 rows; the words come from load_half_row).  Arithmetic in fp32, in the order of the method's
 // reading: RoPE on channel pairs (2i, 2i+1) with the caller's (cos, sin) of the
 // row's original position, y0 = fmaf(x0, c, -(x1 s)), y1 = fmaf(x0, s, x1 c);
 // the unnormalised Sylvester transform stage by stage (h = 1 .. 32 inside a
 // thread, h = 64 across the thread pair), (a + b, a - b); K rows then scaled by
 // 2^-7 so that Q' . K' = Q . K.  Block scale amax/448, codes E4M3(y * 448/amax).
-__device__ __forceinline__ void transform_encode(const uint16_t* __restrict__ src, const int32_t* rows, int n,
+__device__ __forceinline__ void transform_encode(const uint32_t (&w32)[32], int src_row, int n,
                                  const float2* __restrict__ rope, bool hadamard, bool k_side,
                                  uint8_t* __restrict__ out_rows, float* __restrict__ scale_out, float* red) {
   const int tid = threadIdx.x, r = tid >> 1, p = tid & 1;
   const bool valid = r < n;
   float y[64];
-  if (valid) {
-    const uint16_t* rp = src + (long long)rows[r] * kD + 64 * p;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 u = *reinterpret_cast<const uint4*>(rp + 8 * j);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        y[8 * j + 2 * e] = __uint_as_float(w[e] << 16);
-        y[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) y[i] = 0.0f;
+  for (int e = 0; e < 32; ++e) {
+    y[2 * e] = __uint_as_float(w32[e] << 16);
+    y[2 * e + 1] = __uint_as_float(w32[e] & 0xFFFF0000u);
   }
   if (rope && valid) {
-    const float2* cs = rope + (long long)rows[r] * 64 + 32 * p;
+    const float2* cs = rope + (long long)src_row * 64 + 32 * p;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const float2 c = cs[i];
@@ -217,12 +223,42 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
   if (tid < kBlock) rows[tid] = tid < n ? perm[(long long)bh * N + t * kBlock + tid] : 0;
   __syncthreads();
 
+  // Every load of the block is issued before any is used, so that the K rows,
+  // the V rows and the Q rows (96 KiB) are in flight together: K and Q half rows
+  // into registers, V rows straight into the swizzled LDS tile (global -> LDS
+  // copies; rows past n read as zero through the buffer's record count).
+  const int r = tid >> 1, p = tid & 1;
+  uint32_t kw[32], qw[32];
+  load_half_row(K + (long long)bh * N * kD, rows[r], r < n, p, kw);
+  {
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(V + (long long)bh * N * kD), (short)0, (int)((uint32_t)N * kD * 2u), 0x00020000);
+    const int wave = tid >> 6, lane = tid & 63;
+    uint32_t off[8], src[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) src[j] = (uint32_t)rows[(wave * 8 + j) * 4 + (lane >> 4)];
+    // rows[] is 0 past n: read unconditionally (no branch around the reads)
+    asm volatile("" : "+v"(src[0]), "+v"(src[1]), "+v"(src[2]), "+v"(src[3]), "+v"(src[4]), "+v"(src[5]),
+                 "+v"(src[6]), "+v"(src[7]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {   // 16-byte LDS chunk (wave * 8 + j) * 64 + lane of the tile
+      const int rr = (wave * 8 + j) * 4 + (lane >> 4), m = (lane & 15) ^ ((rr >> 4) & 7);
+      off[j] = rr < n ? src[j] * (kD * 2u) + 16u * m : 0xFFFFFFF0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vr, (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(tile) + (wave * 8 + j) * 1024),
+          16, (int)off[j], 0, 0, 0);
+  }
+  if (Q) load_half_row(Q + (long long)bh * N * kD, t * kBlock + r, r < n, p, qw);
+
   // K: gathered, per-block scale
-  transform_encode(K + (long long)bh * N * kD, rows, n, rope, hadamard != 0, true, k_codes + rowbase * kD,
+  transform_encode(kw, rows[r], n, rope, hadamard != 0, true, k_codes + rowbase * kD,
                    k_scales + (long long)bh * nb + t, red);
 
   // V residual
-  stage_rows(tile, V + (long long)bh * N * kD, rows, n, 256);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (kVFmt == VC_V_E4M3) {
     if (tid < kD) {
@@ -316,12 +352,9 @@ __global__ void __launch_bounds__(256) pre_pass2(const uint16_t* __restrict__ Q,
   __syncthreads();
 
   // Q: original order, per-block scale
-  if (Q) {
-    if (tid < kBlock) rows[tid] = t * kBlock + tid;
-    __syncthreads();
-    transform_encode(Q + (long long)bh * N * kD, rows, n, rope, hadamard != 0, false, q_codes + rowbase * kD,
+  if (Q)
+    transform_encode(qw, t * kBlock + r, n, rope, hadamard != 0, false, q_codes + rowbase * kD,
                      q_scales + (long long)bh * nb + t, red);
-  }
 }
 
 }  // namespace vc

@@ -13,14 +13,17 @@
 //             centroid = (float)((double)sum * 2^-24 / (double)count)
 //
 // Kernels (all on the caller's stream, launched T times for assign/update):
-//   kmeans_init     centroid c <- V[floor(c*N/k)], zero the accumulators, |c|^2
-//   kmeans_assign   labels and counts: one token per lane, four independent FMA
-//                   chains (centroids read through the scalar cache: uniform
-//                   addresses)
-//   kmeans_accum    fixed-point sums: tokens one at a time, lanes over channels,
-//                   into LDS (k <= 64; conflict-free), then one global atomic
-//                   per non-zero partial of the 2048-token block
-//   kmeans_update   new centroids, zero the accumulators, |c|^2
+//   kmeans_init         centroid c <- V[floor(c*N/k)], zero the sums, |c|^2
+//   kmeans_assign_mfma  labels and counts for k <= 64: an int8 MFMA screen with a
+//                       rigorous bound, the fixed-order rule for open tokens
+//   kmeans_assign       labels and counts for k > 64: one token per lane, four
+//                       independent FMA chains (centroids through the scalar
+//                       cache: uniform addresses)
+//   kmeans_accum        fixed-point sums: tokens one at a time, lanes over
+//                       channels, into LDS (k <= 64; conflict-free), then one
+//                       global atomic per non-zero partial of the 4096-token
+//                       block; after the first pass only tokens whose label moved
+//   kmeans_update       new centroids from the persistent sums, zero the counts, |c|^2
 //   sort_hist / sort_scan / sort_scatter   stable counting sort by label
 #include <type_traits>
 
@@ -47,6 +50,7 @@ struct KmWork {
   long long* sums; // [BH, k, 128]
   unsigned* counts;// [BH, k]
   int32_t* labels; // [BH, N]
+  int32_t* prev;   // [BH, N] labels as of the last accumulation
   int32_t* hist;   // [BH, nchunks, k]
 };
 
@@ -57,20 +61,37 @@ __device__ float centroid_norm(const float* c) {
   return acc;
 }
 
-// Two int8 digits of a value x of a row with scale s = max|row| / 127:
-// h = RNE(x / s) (|h| <= 127), then l = RNE((x - h s) / (s / 254)) (|l| <= 127),
-// so |x - (h s + l s / 254)| <= (s / 254) (1/2 + 2^-14).
-__device__ __forceinline__ void two_digits(float x, float s, float inv_s, int& h, int& l) {
-  const float hf = fminf(fmaxf(__builtin_rintf(x * inv_s), -127.0f), 127.0f);
-  const float e = __builtin_fmaf(-hf, s, x);
-  const float lf = fminf(fmaxf(__builtin_rintf(e * (254.0f * inv_s)), -127.0f), 127.0f);
-  h = (int)hf;
-  l = (int)lf;
+// Two int8 digits of a value x of a row with max |row| = m: with inv = fl(32512 / m),
+// X = RNE(x * inv) satisfies |X| <= 32512 and |x - X / inv| <= 1 / (2 inv).  One
+// fused multiply-add t = fl(x * inv + (1.5 * 2^23 + 128)) rounds x * inv to X
+// and leaves X + 128 in the low 16 bits of t (two's complement; t stays in
+// [2^23, 2^24), where the float spacing is 1): byte 1 of t is the signed high
+// digit h, byte 0 is l + 128, and X = 256 h + l with h in [-127, 127], l in
+// [-128, 127].
+constexpr float kDigitMagic = 12583040.0f;   // 1.5 * 2^23 + 128
+__device__ __forceinline__ uint32_t digit_word(float x, float inv) {
+  return __float_as_uint(__builtin_fmaf(x, inv, kDigitMagic));
+}
+// high digits (byte 1) and low digits (byte 0 ^ 0x80) of four digit words
+__device__ __forceinline__ void digit_bytes(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3, uint32_t& hi,
+                                            uint32_t& lo) {
+  const uint32_t a = __builtin_amdgcn_perm(t1, t0, 0x05010400u);   // t0.b0 t1.b0 t0.b1 t1.b1
+  const uint32_t b = __builtin_amdgcn_perm(t3, t2, 0x05010400u);   // t2.b0 t3.b0 t2.b1 t3.b1
+  hi = __builtin_amdgcn_perm(b, a, 0x07060302u);                   // t0.b1 t1.b1 t2.b1 t3.b1
+  lo = __builtin_amdgcn_perm(b, a, 0x05040100u) ^ 0x80808080u;     // t0.b0 t1.b0 t2.b0 t3.b0
 }
 
-// value of lane l ^ 32
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
-__device__ __forceinline__ int swap_halves(int x) { return __shfl_xor(x, 32); }
+// value of lane l ^ 32 (V_PERMLANE32_SWAP, no LDS permute): with both operands
+// x, each lane gets its own value in one result and that of lane l ^ 32 in the
+// other, so the one that differs from x is the other half's (if neither
+// differs, the two values are equal)
+__device__ __forceinline__ int swap_halves(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return (int)(r[0] != (unsigned)x ? r[0] : r[1]);
+}
+__device__ __forceinline__ float swap_halves(float x) {
+  return __int_as_float(swap_halves(__float_as_int(x)));
+}
 
 __global__ void __launch_bounds__(kD) kmeans_init(const uint16_t* __restrict__ V, int N, int k,
                                                   KmWork w) {
@@ -160,30 +181,28 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign(const uint16_t* 
 // Screened assignment (k <= 64).  The distance of the fixed-order fp32 rule is
 // the arbiter; a screen finds every token whose argmin it decides.
 //  * The token's bf16 values and every centroid are coded as two int8 digits
-//    with one scale s per row (s = max|row| / 127): x ~ s h + (s / 254) l,
-//    error <= (s / 254) (1/2 + 2^-14).  V_MFMA_I32_32X32X32_I8 gives the exact
-//    integer dot products D_hh of the high digits and D_x = D_hl + D_lh of the
-//    mixed ones; the low-low term is dropped.
-//  * The screened score s_a = cc - 2 s_v s_c (254 D_hh + D_x) / 254 differs
-//    from the fixed-order score s_o by at most
-//    B = 1.002 [ (s_c |v|_1 + s_v |c|_1) / 254      (digit errors, times 2)
-//              + 64.02 s_v s_c                      (dropped low-low term: 2 * 128 * 127^2 / 254^2)
-//              + (2^-15 + 2^-17) |v|_1 max|c| ]     (fp32 chain of s_o; rounding of s_a)
+//    per value with one factor per row (digit_word): x = (256 h + l) r + d with
+//    r = 1 / fl(32512 / max|row|) and |d| <= r / 2.  V_MFMA_I32_32X32X32_I8 gives
+//    the exact integer dot products D_hh of the high digits and D_x = D_hl + D_lh
+//    of the mixed ones; the low-low term (|D_ll| <= 2^21) is dropped.
+//  * The screened score s_a = cc - 512 r_v r_c (256 D_hh + D_x) differs from the
+//    fixed-order score s_o by at most
+//    B = 1.002 [ r_c |v|_1 + r_v |c|_1               (digit errors, times 2)
+//              + (2^22 + 64) r_v r_c                 (dropped low-low term and the digit cross term)
+//              + (2^-15 + 2^-17) |v|_1 max|c| ]      (fp32 chain of s_o; rounding of s_a)
 //        + 2^-19 |cc|                               (rounding of s_a and of the comparison)
 //    where the factor 1.002 covers the evaluation of B.  Per centroid, B =
-//    A_c |v|_1 + s_v B_c + C_c with A_c, B_c, C_c from an LDS table.
+//    A_c |v|_1 + r_v B_c + C_c with A_c, B_c, C_c from an LDS table.
 //  * With U = min_c (s_a + B), only centroids with s_a - B <= U can be the
 //    argmin.  A token with one such centroid takes it (all others score
 //    strictly more); any other token is recomputed with the fixed-order
 //    chain itself: lane c takes centroid c, the lowest index wins ties.  So is
 //    every token, and every centroid counts as a candidate, whose max |x| lies
 //    outside [2^-40, 2^40] (0 aside), where the rounding terms would not hold.
-//  * Token digits: the high one from the 1.5 * 2^23 rounding trick (its byte is
-//    the low byte of the sum), the low one rounded to a byte q + 128 by
-//    V_CVT_PK_U8_F32; one XOR per word turns bytes q + 128 into int8.
 // Lane layout: lanes l and l + 32 share token l % 32 (channel halves of each
 // 32-channel slice: the B operand of the MFMA); the output rows (centroids)
 // 8(r/4) + 4(l/32) + r%4 of each 32-centroid block stay in lane l.
+template <int kNB>   // 32-centroid blocks: (k + 31) / 32
 __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint16_t* __restrict__ V, int N, int k,
                                                                       KmWork w) {
   __shared__ float Ct[kD][kLdsSumsMaxK + 1];   // centroids transposed (zero past k), padded against bank conflicts
@@ -191,8 +210,8 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
   __shared__ __align__(16) uint4 cqs[2][4][2][kLdsSumsMaxK];
   __shared__ float ccs[kLdsSumsMaxK];      // |c|^2, +inf past k
   __shared__ float part[2][4][kLdsSumsMaxK];
-  __shared__ float scs[kLdsSumsMaxK];      // s_c
-  __shared__ float4 tabA[kLdsSumsMaxK];    // {-2 s_c / 254, A_c, B_c, cc} (zero and +inf past k)
+  __shared__ float invs[kLdsSumsMaxK];     // fl(32512 / max|c|), 0 for a zero centroid
+  __shared__ float4 tabA[kLdsSumsMaxK];    // {-512 r_c, A_c, B_c, cc} (zero and +inf past k)
   __shared__ float tabC[kLdsSumsMaxK];     // C_c
   __shared__ unsigned cnt[kLdsSumsMaxK];
   const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, g = lane >> 5, col = lane & 31;
@@ -221,13 +240,14 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
     const int c = tid;
     const float l1 = (((part[0][0][c] + part[0][1][c]) + part[0][2][c]) + part[0][3][c]) * (1.0f + 0x1p-15f);
     const float mx = fmaxf(fmaxf(part[1][0][c], part[1][1][c]), fmaxf(part[1][2][c], part[1][3][c]));
-    const float sc = mx / 127.0f;
+    const float inv_c = mx > 0.0f ? 32512.0f / mx : 0.0f;
+    const float rc = mx > 0.0f ? 1.0f / inv_c : 0.0f;
     // a centroid outside the screened range is a candidate for every token
     const bool ok = mx == 0.0f || (mx >= 0x1p-40f && mx <= 0x1p40f);
-    scs[c] = sc;
+    invs[c] = inv_c;
     if (c < k) {
-      tabA[c] = make_float4((-2.0f / 254.0f) * sc, 1.002f * (sc * (1.0f / 254.0f) + (0x1p-15f + 0x1p-17f) * mx),
-                            1.002f * (l1 * (1.0f / 254.0f) + 64.02f * sc), ccs[c]);
+      tabA[c] = make_float4(-512.0f * rc, 1.002f * (rc + (0x1p-15f + 0x1p-17f) * mx),
+                            1.002f * (l1 + 4194368.0f * rc), ccs[c]);   // 2^22 + 64
       tabC[c] = ok ? 0x1p-19f * fabsf(ccs[c]) : __builtin_inff();
     } else {
       tabA[c] = make_float4(0.0f, 0.0f, 0.0f, __builtin_inff());
@@ -237,23 +257,18 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
   __syncthreads();
   for (int idx = tid; idx < 4 * 2 * kLdsSumsMaxK; idx += kAssignThreads) {
     const int c = idx % kLdsSumsMaxK, gg = (idx / kLdsSumsMaxK) % 2, s4 = idx / (2 * kLdsSumsMaxK);
-    const float sc = scs[c], inv_c = sc > 0.0f ? 1.0f / sc : 0.0f;
+    const float inv_c = invs[c];
     uint32_t hw[4], lw[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      hw[q] = lw[q] = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int h, l;
-        two_digits(Ct[32 * s4 + 16 * gg + 4 * q + e][c], sc, inv_c, h, l);
-        hw[q] |= (uint32_t)(h & 0xFF) << (8 * e);
-        lw[q] |= (uint32_t)(l & 0xFF) << (8 * e);
-      }
+      const float* col = &Ct[32 * s4 + 16 * gg + 4 * q][c];
+      digit_bytes(digit_word(col[0], inv_c), digit_word(col[kLdsSumsMaxK + 1], inv_c),
+                  digit_word(col[2 * (kLdsSumsMaxK + 1)], inv_c), digit_word(col[3 * (kLdsSumsMaxK + 1)], inv_c),
+                  hw[q], lw[q]);
     }
     cqs[0][s4][gg][c] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     cqs[1][s4][gg][c] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
-  const int nblk = (k + 31) >> 5;
   __syncthreads();
 
   const int wave = tid >> 6;
@@ -296,49 +311,41 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
     const float vmax = fmaxf(vmax_l, swap_halves(vmax_l));
     l1 = (l1 + swap_halves(l1)) * (1.0f + 0x1p-15f);
     const bool screenable = vmax == 0.0f || (vmax >= 0x1p-40f && vmax <= 0x1p40f);
-    const float sv = vmax / 127.0f;
-    const float inv = vmax > 0.0f ? 1.0f / sv : 0.0f;
-    const float inv254 = 254.0f * inv;
-    // Token digits.  High: t = fl(x / s + 1.5 * 2^23 + 128) rounds x / s to the
-    // nearest integer h (ties to even) in one step, t's low byte is h + 128 and
-    // t - (1.5 * 2^23 + 128) is h exactly.  Low: l = RNE(fl(e * 254/s + 128)) - 128
-    // with e = fl(x - h s), rounded to a byte by V_CVT_PK_U8_F32.  Both stay in
-    // [-127, 127] because |x / s| <= 127 (up to rounding), and |x - h s - l s / 254|
-    // <= (s / 254) (1/2 + 2^-14).  One XOR per word turns bytes q + 128 into int8.
-    constexpr float kMagic = 12583040.0f;   // 1.5 * 2^23 + 128
+    // inv need not be the correctly rounded quotient: any inv with vmax * inv
+    // below 32639.5 keeps both digits in range, and r_v below is 1 / inv itself
+    // (V_RCP_F32, within the 1.002 margin of the bound)
+    const float inv = vmax > 0.0f ? 32512.0f * __builtin_amdgcn_rcpf(vmax) : 0.0f;
+    const float sv = vmax > 0.0f ? __builtin_amdgcn_rcpf(inv) : 0.0f;   // r_v
+    // token digits (digit_word): one fused multiply-add per value, the bytes
+    // gathered four values at a time
     v4i bop[2][4];   // [high/low][slice]
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         uint32_t tw[4];
-        uint32_t wl = 0u;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ee = 4 * q4 + e;
           const uint32_t wd = raw[s4][ee >> 1];
-          const float x = __uint_as_float((ee & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
-          const float t = __builtin_fmaf(x, inv, kMagic);
-          const float r = __builtin_fmaf(-(t - kMagic), sv, x);
-          tw[e] = __float_as_uint(t);
-          wl = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(r, inv254, 128.0f), e, wl);
+          tw[e] = digit_word(__uint_as_float((ee & 1) ? (wd & 0xFFFF0000u) : (wd << 16)), inv);
         }
-        const uint32_t wh = __builtin_amdgcn_perm(tw[1], tw[0], 0x0C0C0400u) |
-                            __builtin_amdgcn_perm(tw[3], tw[2], 0x04000C0Cu);
-        bop[0][s4][q4] = (int)(wh ^ 0x80808080u);
-        bop[1][s4][q4] = (int)(wl ^ 0x80808080u);
+        uint32_t wh, wl;
+        digit_bytes(tw[0], tw[1], tw[2], tw[3], wh, wl);
+        bop[0][s4][q4] = (int)wh;
+        bop[1][s4][q4] = (int)wl;
       }
     // prefetch of the next group, unconditional (the last group reloads itself)
     // so that the compiler keeps one copy of the row registers
     load_group(grp + 1 < kMTokWG / 4 / 32 && t0 + 32 < N ? t0 + 32 : t0);
-    // screened scores s_a = cc - 2 s_v s_c D / 254 (D = 254 D_hh + D_x) of
+    // screened scores s_a = cc - 512 r_v r_c D (D = 256 D_hh + D_x) of
     // centroids 32b + 8(r/4) + 4g + r%4 (this lane's rows) with their bounds:
     // keep s_a - B, and U = min (s_a + B) over the token's centroids
     float lo[2][16];
     float U = __builtin_inff();
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      if (b < nblk) {
+      if (b < kNB) {
         v16i acc, accx;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = accx[r] = 0;
@@ -355,8 +362,8 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
         for (int r = 0; r < 16; ++r) {
           const int c = 32 * b + 8 * (r >> 2) + 4 * g + (r & 3);
           const float4 ta = tabA[c];
-          // |254 D_hh + D_x| < 2^30: the 24-bit multiply-add is exact
-          const int di = __mul24(acc[r], 254) + accx[r];
+          // |256 D_hh + D_x| < 2^30 (|D_hh| < 2^21, |D_x| < 2^22): exact in int32
+          const int di = acc[r] * 256 + accx[r];
           const float sa = __builtin_fmaf((float)di, sv * ta.x, ta.w);
           const float bd = __builtin_fmaf(ta.y, l1, __builtin_fmaf(ta.z, sv, tabC[c]));
           lo[b][r] = sa - bd;
@@ -388,13 +395,16 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
     while (open) {
       const int tl = __builtin_ctzll(open);
       open &= open - 1;
-      const uint16_t* tp = V + ((long long)bh * N + t0 + tl) * kD;
+      // the token's row in one coalesced load (lane l: channels 2l, 2l + 1); the
+      // chain takes each value from its lane with V_READLANE (a scalar operand)
+      const uint32_t wrow = reinterpret_cast<const uint32_t*>(V + ((long long)bh * N + t0 + tl) * kD)[lane];
       float d = 0.0f;
-      const int c = lane;
-#pragma unroll 8
-      for (int i = 0; i < kD; ++i) {   // fixed order: channel 0..127
-        const float xi = bf16_bits_to_f32(tp[i]);
-        d = __builtin_fmaf(xi, c < k ? Ct[i][c] : 0.0f, d);
+      const int c = lane;   // Ct is zero past k
+#pragma unroll 16
+      for (int i2 = 0; i2 < kD / 2; ++i2) {   // fixed order: channel 0..127
+        const uint32_t wv = __builtin_amdgcn_readlane(wrow, i2);
+        d = __builtin_fmaf(__uint_as_float(wv << 16), Ct[2 * i2][c], d);
+        d = __builtin_fmaf(__uint_as_float(wv & 0xFFFF0000u), Ct[2 * i2 + 1][c], d);
       }
       float sc = c < k ? __builtin_fmaf(-2.0f, d, ccs[c]) : __builtin_inff();
       int bi = c;
@@ -427,6 +437,52 @@ __global__ void __launch_bounds__(kAssignThreads) kmeans_assign_mfma(const uint1
 // that both adds of a token hit 64 consecutive 8-byte slots of the token's
 // cluster row (slot h*64 + l holds channel 2l + h); they never collide.  The
 // integer adds are order-free, so any split of the tokens gives the same sums.
+// The sums persist across iterations: the first pass (kmeans_accum) adds every
+// token; each later pass (kmeans_accum_moved) adds only the tokens whose label
+// moved since the last pass to their new cluster and subtracts them from their
+// old one, which leaves the same integers as a full recount.  Both passes end
+// by recording the labels they accounted for.
+
+// rint(v * 2^24) of the two channels of a row word, added to (sign +1) or
+// subtracted from (sign -1) cluster c's partials.  The int32 conversion is exact
+// when |v| < 128 (largest bf16 below 128: 127.5 * 2^24 < 2^31); the float ->
+// int64 sequence gives the same integers for any finite v.
+template <bool kLdsSums, bool kSmall>
+__device__ __forceinline__ void add_row_word(uint32_t word, int c, bool negate, int ln,
+                                             unsigned long long* psum, unsigned long long* gs) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float xv = __uint_as_float(h ? (word & 0xFFFF0000u) : (word << 16));
+    const float r = __builtin_rintf(xv * 16777216.0f);
+    long long qv = kSmall ? (long long)(int)r : (long long)r;
+    if (negate) qv = -qv;
+    if (kLdsSums) atomicAdd(&psum[c * kD + 64 * h + ln], (unsigned long long)qv);
+    else atomicAdd(&gs[(long long)c * kD + 2 * ln + h], (unsigned long long)qv);
+  }
+}
+
+// |v| < 128 (and finite) for both channels of every word, over the wavefront
+template <int kN>
+__device__ __forceinline__ bool words_small(const uint32_t (&raw)[kN]) {
+  u16x2 mb = {0, 0};
+#pragma unroll
+  for (int b = 0; b < kN; ++b) mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, raw[b] & 0x7FFF7FFFu));
+  return __all(mb[0] < 0x4300u && mb[1] < 0x4300u);
+}
+
+template <bool kLdsSums>
+__device__ __forceinline__ void flush_partials(int k, int tid, const unsigned long long* psum,
+                                               unsigned long long* gs) {
+  if (kLdsSums) {
+    __syncthreads();
+    for (int idx = tid; idx < k * kD; idx += kAccThreads) {
+      const unsigned long long v = psum[idx];
+      const int c = idx / kD, slot = idx % kD;
+      if (v) atomicAdd(&gs[(long long)c * kD + 2 * (slot & 63) + (slot >> 6)], v);
+    }
+  }
+}
+
 template <bool kLdsSums>
 __global__ void __launch_bounds__(kAccThreads) kmeans_accum(const uint16_t* __restrict__ V, int N, int k,
                                                               KmWork w) {
@@ -455,39 +511,81 @@ __global__ void __launch_bounds__(kAccThreads) kmeans_accum(const uint16_t* __re
       cl[b] = j < N ? lab[jj] : -1;   // uniform address: a scalar load
       raw[b] = V32[jj * (kD / 2) + ln];
     }
-    // rint(v * 2^24) is exact in int32 when every |v| of the batch is below 128
-    // (largest bf16 below 128: 127.5 * 2^24 < 2^31): one 32-bit conversion then,
-    // instead of the float -> int64 sequence.  Same integers either way.
-    u16x2 mb = {0, 0};
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b)
-      mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, raw[b] & 0x7FFF7FFFu));
-    const bool small = __all(mb[0] < 0x4300u && mb[1] < 0x4300u);   // |v| < 128, no inf or NaN
     auto add_batch = [&](auto small_tag) {
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        if (cl[b] < 0) continue;   // beyond N (uniform across the wavefront)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float xv = __uint_as_float(h ? (raw[b] & 0xFFFF0000u) : (raw[b] << 16));
-          const float r = __builtin_rintf(xv * 16777216.0f);
-          const long long qv = decltype(small_tag)::value ? (long long)(int)r : (long long)r;
-          if (kLdsSums) atomicAdd(&psum[cl[b] * kD + 64 * h + ln], (unsigned long long)qv);
-          else atomicAdd(&gs[(long long)cl[b] * kD + 2 * ln + h], (unsigned long long)qv);
-        }
-      }
+      for (int b = 0; b < kBatch; ++b)
+        if (cl[b] >= 0)   // not beyond N (uniform across the wavefront)
+          add_row_word<kLdsSums, decltype(small_tag)::value>(raw[b], cl[b], false, ln, psum, gs);
     };
-    if (small) add_batch(std::true_type{});
+    if (words_small(raw)) add_batch(std::true_type{});
     else add_batch(std::false_type{});
   }
-  if (kLdsSums) {
-    __syncthreads();
-    for (int idx = tid; idx < k * kD; idx += kAccThreads) {
-      const unsigned long long v = psum[idx];
-      const int c = idx / kD, slot = idx % kD;
-      if (v) atomicAdd(&gs[(long long)c * kD + 2 * (slot & 63) + (slot >> 6)], v);
-    }
+  int32_t* __restrict__ prv = w.prev + (long long)bh * N;
+  for (int q = ln; q < kPerWave; q += 64) {
+    const long long j = j_begin + q;
+    if (j < N) prv[j] = lab[j];
   }
+  flush_partials<kLdsSums>(k, tid, psum, gs);
+}
+
+// The later passes: each wavefront compares the labels of its 256 tokens with
+// the recorded ones (coalesced loads, one ballot per 64 tokens) and reads the
+// rows of the moved tokens only, eight at a time.
+template <bool kLdsSums>
+__global__ void __launch_bounds__(kAccThreads) kmeans_accum_moved(const uint16_t* __restrict__ V, int N, int k,
+                                                                    KmWork w) {
+  extern __shared__ __align__(16) unsigned long long psum[];   // [k][128] when kLdsSums
+  const int bh = blockIdx.y, tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), ln = tid & 63;
+  if (kLdsSums)
+    for (int idx = tid; idx < k * kD; idx += kAccThreads) psum[idx] = 0ull;
+  __syncthreads();
+  unsigned long long* gs = reinterpret_cast<unsigned long long*>(w.sums) + (long long)bh * k * kD;
+  const int32_t* __restrict__ lab = w.labels + (long long)bh * N;
+  int32_t* __restrict__ prv = w.prev + (long long)bh * N;
+  const uint32_t* __restrict__ V32 = reinterpret_cast<const uint32_t*>(V + (long long)bh * N * kD);
+  constexpr int kPerWave = kAccTok / (kAccThreads / 64);
+  const long long j_begin = (long long)blockIdx.x * kAccTok + (long long)wv * kPerWave;
+  int nl[kPerWave / 64], ol[kPerWave / 64];
+#pragma unroll
+  for (int q = 0; q < kPerWave / 64; ++q) {
+    const long long j = j_begin + 64 * q + ln;
+    nl[q] = j < N ? lab[j] : 0;
+    ol[q] = j < N ? prv[j] : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < kPerWave / 64; ++q) {
+    unsigned long long m = __ballot(nl[q] != ol[q]);
+    while (m) {   // uniform
+      uint32_t raw[8];
+      int cn[8], co[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        cn[u] = -1;
+        co[u] = -1;
+        raw[u] = 0u;
+        if (m) {
+          const int tl = __builtin_ctzll(m);
+          m &= m - 1;
+          cn[u] = __builtin_amdgcn_readlane(nl[q], tl);
+          co[u] = __builtin_amdgcn_readlane(ol[q], tl);
+          raw[u] = V32[(j_begin + 64 * q + tl) * (kD / 2) + ln];
+        }
+      }
+      auto add_moved = [&](auto small_tag) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (cn[u] >= 0) {   // uniform
+            add_row_word<kLdsSums, decltype(small_tag)::value>(raw[u], cn[u], false, ln, psum, gs);
+            add_row_word<kLdsSums, decltype(small_tag)::value>(raw[u], co[u], true, ln, psum, gs);
+          }
+      };
+      if (words_small(raw)) add_moved(std::true_type{});
+      else add_moved(std::false_type{});
+    }
+    const long long j = j_begin + 64 * q + ln;
+    if (j < N && nl[q] != ol[q]) prv[j] = nl[q];
+  }
+  flush_partials<kLdsSums>(k, tid, psum, gs);
 }
 
 __global__ void __launch_bounds__(kD) kmeans_update(int k, KmWork w) {
@@ -501,7 +599,6 @@ __global__ void __launch_bounds__(kD) kmeans_update(int k, KmWork w) {
     v = (float)((s * 0x1p-24) / (double)n);
     w.cent[ci] = v;
   }
-  w.sums[ci] = 0;
   row[i] = v;
   __syncthreads();
   if (i == 0) {
@@ -603,7 +700,7 @@ __global__ void __launch_bounds__(256) sort_scatter(int N, int k, int nchunks, K
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct KmLayout {
-  size_t cent, cc, sums, counts, labels, hist, total;
+  size_t cent, cc, sums, counts, labels, prev, hist, total;
 };
 
 static KmLayout km_layout(long long BH, long long N, int k) {
@@ -615,6 +712,7 @@ static KmLayout km_layout(long long BH, long long N, int k) {
   L.sums = o;   o += align256(sizeof(long long) * BH * k * kD);
   L.counts = o; o += align256(sizeof(unsigned) * BH * k);
   L.labels = o; o += align256(sizeof(int32_t) * BH * N);
+  L.prev = o;   o += align256(sizeof(int32_t) * BH * N);
   L.hist = o;   o += align256(sizeof(int32_t) * BH * nchunks * k);
   L.total = o;
   return L;
@@ -645,6 +743,7 @@ extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, i
   w.sums = reinterpret_cast<long long*>(ws + L.sums);
   w.counts = reinterpret_cast<unsigned*>(ws + L.counts);
   w.labels = labels ? labels : reinterpret_cast<int32_t*>(ws + L.labels);
+  w.prev = reinterpret_cast<int32_t*>(ws + L.prev);
   w.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int nchunks = (N + kSortChunk - 1) / kSortChunk;
@@ -653,23 +752,34 @@ extern "C" int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, i
   const dim3 gA((N + kTokPerWG - 1) / kTokPerWG, (unsigned)BH);
   const dim3 gS((N + kAccTok - 1) / kAccTok, (unsigned)BH);
   // dynamic LDS above the default limit (cheap; set on every call, no state kept)
-  if (lds_sums)
+  if (lds_sums) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kmeans_accum<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kmeans_accum_moved<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  }
   hipLaunchKernelGGL(kmeans_init, dim3(k, (unsigned)BH), dim3(kD), 0, st, V, N, k, w);
   const dim3 gM((N + kMTokWG - 1) / kMTokWG, (unsigned)BH);
   for (int it = 0; it < iters; ++it) {
-    if (k <= kLdsSumsMaxK)   // screened int8 MFMA pass with a fixed-order recheck
-      hipLaunchKernelGGL(kmeans_assign_mfma, gM, dim3(kAssignThreads), 0, st, V, N, k, w);
-    else
+    if (k <= kLdsSumsMaxK) {   // screened int8 MFMA pass with a fixed-order recheck
+      if (k > 32)
+        hipLaunchKernelGGL(kmeans_assign_mfma<2>, gM, dim3(kAssignThreads), 0, st, V, N, k, w);
+      else
+        hipLaunchKernelGGL(kmeans_assign_mfma<1>, gM, dim3(kAssignThreads), 0, st, V, N, k, w);
+    } else
       hipLaunchKernelGGL(kmeans_assign, gA, dim3(kAssignThreads), 0, st, V, N, k, w);
     // the labels of the last assignment give the permutation; the update after
     // it only matters when the caller asks for the centroids
     if (it + 1 == iters && !centroids) break;
-    if (lds_sums)
+    // the first pass counts every token, later passes only the moved ones
+    if (lds_sums && it == 0)
       hipLaunchKernelGGL(kmeans_accum<true>, gS, dim3(kAccThreads), lds, st, V, N, k, w);
-    else
+    else if (lds_sums)
+      hipLaunchKernelGGL(kmeans_accum_moved<true>, gS, dim3(kAccThreads), lds, st, V, N, k, w);
+    else if (it == 0)
       hipLaunchKernelGGL(kmeans_accum<false>, gS, dim3(kAccThreads), 0, st, V, N, k, w);
+    else
+      hipLaunchKernelGGL(kmeans_accum_moved<false>, gS, dim3(kAccThreads), 0, st, V, N, k, w);
     hipLaunchKernelGGL(kmeans_update, dim3(k, (unsigned)BH), dim3(kD), 0, st, k, w);
   }
   hipLaunchKernelGGL(sort_hist, dim3(nchunks, (unsigned)BH), dim3(256), sizeof(unsigned) * k, st, N, k,
