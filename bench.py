@@ -241,6 +241,58 @@ def cpu_baseline(Q, K, V, c, scale):
     }
 
 
+def prep_bytes(B, H, N):
+    """Algorithmic HBM bytes of one preprocessing call: V read twice, K and Q once
+    (bf16), the permutation twice, three u8 code tensors, the block means and
+    scales written."""
+    nb = -(-N // 128)
+    per_head = 4 * N * 256 + 2 * N * 4 + 3 * nb * 128 * 128 + nb * 128 * 2 + 2 * nb * 4 + 128 * 4
+    return B * H * per_head
+
+
+def hbm_streams(vc, stream, reps=5):
+    """Plain HBM streams of the probe hook (1 GiB of 16-byte words each): the
+    bandwidth a read-only, a copy and a two-reads-per-write pass reach on this GPU
+    (the roof of the memory-bound preprocessing, which reads twice what it writes)."""
+    import torch
+    n = 1 << 26
+    a = torch.ones(2 * n * 4, dtype=torch.int32, device="cuda")
+    b = torch.empty(n * 4, dtype=torch.int32, device="cuda")
+    o = torch.empty(2048 * 256, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, what, nbytes, dst in (("read", "hbm_read", 2 * n * 16, o), ("copy", "hbm_copy", 2 * n * 16, b),
+                                    ("read2_write1", "hbm_read2_write1", 3 * n * 16, b)):
+        count = 2 * n if what == "hbm_read" else n
+        ms = timed(lambda: vc.device_probe(what, a, dst, count), reps, stream)
+        res[name] = round(nbytes / (ms * 1e-3) / 1e12, 3)
+    del a, b, o
+    return res
+
+
+def library_sdpa_ms(Qd, Kd, Vd, reps=2):
+    """PyTorch's own bf16 flash attention (scaled_dot_product_attention restricted
+    to its flash backend, no math fallback) at the same shape, as a library
+    reference point for the in-repo bf16 kernel; None if the backend is missing."""
+    import torch
+    import torch.nn.functional as F
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        q, k, v = (t.view(torch.bfloat16) if t.dtype != torch.bfloat16 else t for t in (Qd, Kd, Vd))
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            F.scaled_dot_product_attention(q, k, v)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                F.scaled_dot_product_attention(q, k, v)
+            e1.record()
+            e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+    except Exception as exc:   # backend not built into this torch
+        print(f"[bench] library SDPA unavailable: {type(exc).__name__}: {exc}", file=sys.stderr, flush=True)
+        return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -323,6 +375,9 @@ def main():
     with ClockSampler() as clk:
         ms_attn = timed(lambda: vc.attn_fp8_fwd(prep, scale, "expcast", out=out), args.kernel_reps, stream)
     ms_bf16 = timed(lambda: vc.attn_bf16_fwd(Qd, Kd, Vd, scale, out=out), 3, stream)
+    ms_sdpa = library_sdpa_ms(Qd, Kd, Vd)
+    streams = hbm_streams(vc, stream)
+    print(f"[bench] library SDPA {ms_sdpa} ms; HBM streams TB/s {streams}", file=sys.stderr, flush=True)
     ablation = p_path_ablation(vc, W, 5, stream, preps={WORKLOAD: prep})
     print(f"[bench] P-path ablation: {json.dumps(ablation)}", file=sys.stderr, flush=True)
     print(f"[bench] group {ms_group:.2f} ms, preprocess {ms_prep:.2f} ms, attention {ms_attn:.2f} ms, "
@@ -366,6 +421,13 @@ def main():
         "p_path_ablation": ablation,
         "bf16_comparator": {"ms": round(ms_bf16, 3), "tflops": round(flops / (ms_bf16 * 1e-3) / 1e12, 1),
                             "speedup_of_fp8_kernel": round(ms_bf16 / ms_attn, 3)},
+        "library_bf16_sdpa_flash": None if ms_sdpa is None else {
+            "ms": round(ms_sdpa, 3), "tflops": round(flops / (ms_sdpa * 1e-3) / 1e12, 1),
+            "speedup_of_fp8_kernel": round(ms_sdpa / ms_attn, 3)},
+        # algorithmic bytes of the preprocessing (pass 1 reads V; pass 2 reads K, V, Q
+        # and writes three code tensors) over its time, next to the plain streams
+        "preprocess_hbm_tbs": round(prep_bytes(B, H, N) / (ms_prep * 1e-3) / 1e12, 3),
+        "hbm_stream_tbs": streams,
         "fidelity_rel_l2_vs_exact_fp32": {"attn_fp8_expcast": float(f"{fid_fp8:.4e}"),
                                           "attn_bf16": float(f"{fid_bf16:.4e}"), "rows": fid_rows},
         # grouping cadence of the pages (first quarter of the denoising steps, each

@@ -3,7 +3,8 @@
 // matrix instructions' accumulation, the rounding and range of the two byte
 // conversions, the accuracy of the hardware exp2); this entry point runs each
 // instruction alone so that tests can record those facts against exact
-// arithmetic on the host.
+// arithmetic on the host.  Three plain HBM streams (read only, copy, two reads
+// per write) measure the bandwidth the memory-bound passes can reach.
 #include "vc_common.h"
 
 namespace vc {
@@ -65,6 +66,30 @@ __global__ void __launch_bounds__(64) probe_mfma(const uint8_t* in, float* out, 
   }
 }
 
+// HBM streams over n 16-byte words, 2048 workgroups of 256 threads striding the
+// array: read only (what = 5: in [n], one XOR per thread to out [2048 * 256]),
+// copy (what = 6: in [n] -> out [n]), two reads per write (what = 7: out[i] =
+// in[i] ^ in[i + n], in [2n], out [n]).
+constexpr int kStreamGrid = 2048;
+__global__ void __launch_bounds__(256) probe_read(const uint4* __restrict__ a, long long n, uint32_t* __restrict__ out) {
+  uint32_t x = 0u;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const uint4 v = a[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = x;
+}
+__global__ void __launch_bounds__(256) probe_copy(const uint4* __restrict__ a, uint4* __restrict__ b, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) b[i] = a[i];
+}
+__global__ void __launch_bounds__(256) probe_read2_write1(const uint4* __restrict__ a, uint4* __restrict__ b,
+                                                          long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const uint4 u = a[i], v = a[i + n];
+    b[i] = make_uint4(u.x ^ v.x, u.y ^ v.y, u.z ^ v.z, u.w ^ v.w);
+  }
+}
+
 }  // namespace vc
 
 using namespace vc;
@@ -79,6 +104,11 @@ extern "C" int vc_device_probe(int what, const void* in, void* out, int n, void*
     case 2: hipLaunchKernelGGL(probe_exp2, grid, block, 0, st, (const float*)in, (float*)out, n); break;
     case 3: hipLaunchKernelGGL(probe_mfma<32>, dim3((unsigned)n), dim3(64), 0, st, (const uint8_t*)in, (float*)out, n); break;
     case 4: hipLaunchKernelGGL(probe_mfma<16>, dim3((unsigned)n), dim3(64), 0, st, (const uint8_t*)in, (float*)out, n); break;
+    case 5: hipLaunchKernelGGL(probe_read, dim3(kStreamGrid), block, 0, st, (const uint4*)in, (long long)n, (uint32_t*)out); break;
+    case 6: hipLaunchKernelGGL(probe_copy, dim3(kStreamGrid), block, 0, st, (const uint4*)in, (uint4*)out, (long long)n); break;
+    case 7:
+      hipLaunchKernelGGL(probe_read2_write1, dim3(kStreamGrid), block, 0, st, (const uint4*)in, (uint4*)out, (long long)n);
+      break;
     default: return VC_ERR_UNSUPPORTED;
   }
   const hipError_t e = hipGetLastError();

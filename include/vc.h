@@ -270,6 +270,10 @@ int vc_attn_fwd_dump(const uint8_t* q_codes, const float* q_scales,
  *           B u8 [32][64], C fp32 [32][32] per tile; out D fp32 [32][32] per
  *           tile, D = A . B^T + C
  *   what 4  V_MFMA_F32_16X16X128_F8F6F4, E4M3   the same with 16, 16, 128
+ * and three HBM streams over n 16-byte words (2048 workgroups x 256 threads):
+ *   what 5  read only                           in [n] -> out u32 [2048*256]
+ *   what 6  copy                                in [n] -> out [n]
+ *   what 7  two reads per write                 in [2n] -> out [n], out[i] = in[i] ^ in[i+n]
  * Returns VC_ERR_UNSUPPORTED for other `what`, VC_ERR_INVALID_ARG for null
  * pointers or n < 1.
  * ------------------------------------------------------------------------ */
