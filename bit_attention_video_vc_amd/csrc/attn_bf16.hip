@@ -4,8 +4,8 @@
 // (insight article, section "A Faster Kernel Does Not Automatically Mean
 // Faster Generation"; paper digest, results table).  This kernel is the in-repo
 // stand-in on MI355X: bf16 V_MFMA_F32_32X32X16_BF16 for Q.K^T and P.V, online
-// softmax with fp32 exp2, P rounded to bf16 (round to nearest even), row sums
-// accumulated in fp32.
+// softmax with fp32 exp2, P rounded to bf16 (round to nearest even), row sums of
+// the rounded P accumulated in fp32 by a bf16 MFMA.
 //
 // Same organisation as the FP8 kernel: S^T = K.Q^T so each lane holds one
 // query's scores and the bf16 P values are already in the B-operand layout of
@@ -141,6 +141,16 @@ __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[cb][r] = 0.0f;
   float mx = -__builtin_inff(), l = 0.0f;
+  // the row sums of the rounded P (the values the P.V product takes) come from
+  // a 16x16x32 bf16 MFMA per 16-key chunk against a lane-parity ones pattern: the
+  // 16x16x32 operand layout reads the chunk's registers as four 8-key slices
+  // of columns l % 16, and the pattern keeps, in output row i, the slices of
+  // query (i / 4) % 2 * 16 + column, so that lane l ends with query l % 32's sum
+  v8bf ones;
+  {
+    const bool on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
+    ones = as_bf(on ? make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u) : make_uint4(0, 0, 0, 0));
+  }
 
   auto step = [&](const int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
@@ -184,7 +194,7 @@ __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
     mx = mx_new;
     const float nmx = -mx_new;
 
-    float rsum = 0.0f;
+    v4f rs = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -197,7 +207,6 @@ __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
           v2f p;
           p.x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][8 * s2 + 2 * e], a.c0, nmx));
           p.y = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][8 * s2 + 2 * e + 1], a.c0, nmx));
-          rsum += p.x + p.y;
           const v2bf pb = __builtin_convertvector(p, v2bf);   // round to nearest even
           pw[e] = __builtin_bit_cast(uint32_t, pb);
         }
@@ -207,10 +216,10 @@ __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
           const uint4 vv = *reinterpret_cast<const uint4*>(V + kRowB * 32 * cb + lv[2 * m + s2]);
           o[cb] = mfma_bf16(as_bf(vv), pop, o[cb]);
         }
+        rs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, rs, 0, 0, 0);
       }
     }
-    rsum += __shfl_xor(rsum, 32);
-    l += rsum;
+    l += rs[0];
     wait_dma();
     __syncthreads();
   };
