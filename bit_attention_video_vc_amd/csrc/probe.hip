@@ -90,6 +90,37 @@ __global__ void __launch_bounds__(256) probe_read2_write1(const uint4* __restric
   }
 }
 
+// FP8 MFMA throughput (what = 8): n workgroups of 256 threads (one wavefront per
+// SIMD), each wavefront kMfmaIters iterations of four independent
+// V_MFMA_F32_32X32X64_F8F6F4 on register operands taken from `in` (E4M3 bytes,
+// 2 KiB); out [n * 256] receives each thread's accumulator sum, so nothing is
+// optimised away.  131072 FLOP per instruction.
+constexpr int kMfmaIters = 2048;
+__global__ void __launch_bounds__(256) probe_mfma_rate(const uint8_t* __restrict__ in, float* __restrict__ out) {
+  const int tid = threadIdx.x;
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = reinterpret_cast<const int*>(in)[(tid * 8 + i) & 511];
+    b[i] = reinterpret_cast<const int*>(in)[(tid * 5 + i + 7) & 511];
+  }
+  v16f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+  for (int it = 0; it < kMfmaIters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j], 0, 0, 0, 0, 0, 0);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[j][r];
+  out[blockIdx.x * 256 + tid] = sum;
+}
+
 }  // namespace vc
 
 using namespace vc;
@@ -109,6 +140,7 @@ extern "C" int vc_device_probe(int what, const void* in, void* out, int n, void*
     case 7:
       hipLaunchKernelGGL(probe_read2_write1, dim3(kStreamGrid), block, 0, st, (const uint4*)in, (uint4*)out, (long long)n);
       break;
+    case 8: hipLaunchKernelGGL(probe_mfma_rate, dim3((unsigned)n), block, 0, st, (const uint8_t*)in, (float*)out); break;
     default: return VC_ERR_UNSUPPORTED;
   }
   const hipError_t e = hipGetLastError();

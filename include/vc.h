@@ -274,6 +274,10 @@ int vc_attn_fwd_dump(const uint8_t* q_codes, const float* q_scales,
  *   what 5  read only                           in [n] -> out u32 [2048*256]
  *   what 6  copy                                in [n] -> out [n]
  *   what 7  two reads per write                 in [2n] -> out [n], out[i] = in[i] ^ in[i+n]
+ * and the FP8 MFMA throughput:
+ *   what 8  n workgroups x 4 wavefronts, each 2048 x 4 independent
+ *           V_MFMA_F32_32X32X64_F8F6F4 on operands from in (u8 [2048])
+ *                                               -> out fp32 [n*256] (accumulator sums)
  * Returns VC_ERR_UNSUPPORTED for other `what`, VC_ERR_INVALID_ARG for null
  * pointers or n < 1.
  * ------------------------------------------------------------------------ */

@@ -211,3 +211,19 @@ def test_hbm_stream_probes_move_the_right_words(vc):
     vc.device_probe("hbm_read2_write1", a, b, n)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(b.cpu().numpy().view(np.uint32), words[:n] ^ words[n:])
+
+
+def test_mfma_rate_probe_runs_and_is_deterministic(vc):
+    """The FP8 MFMA rate kernel behind bench.py's achievable-peak figure runs to
+    completion and gives the same finite sums twice (4 workgroups)."""
+    _say("device probe: FP8 MFMA rate kernel, 4 workgroups")
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(3)
+    codes = torch.randint(0, 0x40, (2048,), generator=g, dtype=torch.int32).to(torch.uint8).to(dev)
+    out1 = torch.empty(4 * 256, dtype=torch.float32, device=dev)
+    out2 = torch.empty_like(out1)
+    vc.device_probe("mfma_fp8_rate", codes, out1, 4)
+    vc.device_probe("mfma_fp8_rate", codes, out2, 4)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out1).all()
+    assert torch.equal(out1, out2)
