@@ -275,12 +275,11 @@ extern "C" int vc_attn_bf16_fwd(const uint16_t* Q, const uint16_t* K, const uint
   hipLaunchKernelGGL(transpose_v_bf16, dim3(nb, B * H), dim3(256), 0, st, V, N, nb, vt);
   B16Args a{Q, K, vt, out, N, nb, nqb, B * H, score_scale_c0(softmax_scale)};
   const size_t lds = 4u * kTileB;   // 128 KiB: double-buffered K and V^T
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bf16_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr_set = true;
-  }
+  // dynamic LDS above the default limit, set on every call: the attribute is per
+  // device, and a call may run on any device (cheap; no state kept)
+  const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bf16_kernel),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (ea != hipSuccess) return vc_set_hip_error((int)ea);
   hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)(nqb * B * H)), dim3(kB16Threads), lds, st, a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VC_OK : vc_set_hip_error((int)e);
