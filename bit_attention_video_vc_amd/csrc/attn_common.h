@@ -47,7 +47,8 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint8_t* lds_wave_base) 
 // Buffer-resource form of the same copy: the tile base stays in scalar
 // registers (descriptor + soffset) and each lane adds a 32-bit offset, so no
 // per-lane 64-bit address is kept live across a loop.  The descriptor's record
-// count bounds every access: offsets at or past `bytes` read as zero.
+// count bounds the per-lane offset only (a lane offset at or past `bytes` reads
+// zeros); the scalar offset is not checked, so callers keep it inside the record.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

@@ -162,13 +162,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
       dvoff = (uint32_t)(r4 * 64 + 16 * ((lane & 3) ^ ((r4 >> 2) & 3)));
     }
   }
-  // half i (0, 1) of K tile t into buffer buf
+  // half i (0, 1) of K tile t into buffer buf.  The last step asks for tile nb,
+  // which does not exist: it copies tile nb - 1 again into a buffer that is not
+  // read again (the buffer's scalar offset is outside the record-count check,
+  // so it never points past the head's codes)
   auto copy_k = [&](int t, int buf, int i) {
-    dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * (wave + 8 * i), dkoff, (uint32_t)t * kTile + 8192u * i);
+    dma16_buf(krs, (buf ? Ks1 : Ks0) + 1024 * (wave + 8 * i), dkoff, (uint32_t)min(t, nb - 1) * kTile + 8192u * i);
   };
-  // piece i (0, 1) of V tile t into buffer buf: E4M3 the two halves; MXFP4 the
-  // codes, then the E8M0 scales (wavefront 0).  Past the last tile the buffer
-  // resources read zeros into a buffer that is not read again.
+  // piece i (0, 1) of V tile t (t < nb) into buffer buf: E4M3 the two halves;
+  // MXFP4 the codes, then the E8M0 scales (wavefront 0)
   auto copy_v = [&](int t, int buf, int i) {
     if (!kFP4) dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * (wave + 8 * i), dvoff, (uint32_t)t * kTile + 8192u * i);
     else if (i == 0) dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * wave, dvoff, (uint32_t)t * kVTile);
