@@ -220,6 +220,26 @@ def mfma_probe_tflops(vc, stream, reps=3):
     return round(n * 4 * 2048 * 4 * 131072.0 / (ms * 1e-3) / 1e12, 1)
 
 
+def valu_issue_probe(vc):
+    """Per-SIMD issue rates of V_FMA_F32 and V_EXP_F32 with one and two
+    wavefronts per SIMD (the probe hook's issue-rate kernel, one workgroup per
+    CU): the one-wavefront FMA rate as a fraction of the two-wavefront rate, and
+    the cost of an exp relative to an FMA."""
+    import torch
+    n = 256
+    out = torch.zeros(n * 8 * 2, dtype=torch.int64, device="cuda")
+    rate = {}
+    for mode in (0, 1):
+        for active in (4, 8):
+            cfg = torch.tensor([mode, active], dtype=torch.int32, device="cuda")
+            vc.device_probe("valu_rate", cfg, out, n)
+            torch.cuda.synchronize()
+            ticks = out.view(n, 8, 2)[:, :active, 0].double().mean().item()
+            rate[(mode, active // 4)] = (active // 4) * 8 * 4096 / ticks
+    return {"fma_rate_one_wavefront_per_simd_vs_two": round(rate[(0, 1)] / rate[(0, 2)], 3),
+            "exp_cost_vs_fma_two_wavefronts_per_simd": round(rate[(0, 2)] / rate[(1, 2)], 3)}
+
+
 def timed(fn, reps, stream):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -416,6 +436,7 @@ def main():
     ms5 = timed(lambda: vc.attn_fp8_fwd(prep5, scale, "expcast", out=out5), 10, stream)
     del prep5, out5
     mfma_peak = mfma_probe_tflops(vc, stream)
+    valu_probe = valu_issue_probe(vc)
     ms_bf16 = timed(lambda: vc.attn_bf16_fwd(Qd, Kd, Vd, scale, out=out), 3, stream)
     ms_sdpa = library_sdpa_ms(Qd, Kd, Vd)
     streams = hbm_streams(vc, stream)
@@ -466,6 +487,7 @@ def main():
         "head_shard_share": {"heads": H5, "ms": round(ms5, 3),
                              "tflops": round(4.0 * N * N * 128 * H5 * B / (ms5 * 1e-3) / 1e12, 1)},
         "mfma_fp8_probe_tflops": mfma_peak,
+        "valu_issue_probe": valu_probe,
         "sclk_mhz_during_attention": clk.mean(),
         "p_path_ablation": ablation,
         "bf16_comparator": {"ms": round(ms_bf16, 3), "tflops": round(flops / (ms_bf16 * 1e-3) / 1e12, 1),

@@ -271,15 +271,16 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
   // are <= 56, so adding 0x78 to every byte carries nowhere and sets a byte's
   // top bit exactly when its code is >= 8; V_PERM_B32 spreads those top bits
   // (bytes 1, 3 directly, bytes 0, 2 from the copy shifted left by 8) into byte masks
+  auto flush_q = [&](int q) {
+    const uint64_t w64 = ((uint64_t)pk[2 * q + 1] << 32) | pk[2 * q];
+    const uint64_t t = w64 + 0x7878787878787878ull;
+    const uint64_t t8 = t << 8;
+    pk[2 * q] &= __builtin_amdgcn_perm((uint32_t)t8, (uint32_t)t, 0x090B080Au);
+    pk[2 * q + 1] &= __builtin_amdgcn_perm((uint32_t)(t8 >> 32), (uint32_t)(t >> 32), 0x090B080Au);
+  };
   auto flush = [&]() {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint64_t w64 = ((uint64_t)pk[2 * q + 1] << 32) | pk[2 * q];
-      const uint64_t t = w64 + 0x7878787878787878ull;
-      const uint64_t t8 = t << 8;
-      pk[2 * q] &= __builtin_amdgcn_perm((uint32_t)t8, (uint32_t)t, 0x090B080Au);
-      pk[2 * q + 1] &= __builtin_amdgcn_perm((uint32_t)(t8 >> 32), (uint32_t)(t >> 32), 0x090B080Au);
-    }
+    for (int q = 0; q < 8; ++q) flush_q(q);
   };
   // keys at or beyond N of tile t (the last): P byte 0 whatever the score scale
   auto mask_pk = [&](int t) {
@@ -344,46 +345,65 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     // ---- the row sum of tile t-2 joins l ----
     take_rowsum((slot + 2) & 3);
 
-    // ---- stage 1: S^T = K_t . Q^T; beside it the flush of tile t-1's P bytes ----
+    // ---- stage 1: S^T = K_t . Q^T in four chunks, one 32-key block each; beside
+    // a chunk's two MFMAs run the operand reads of the next chunk, a quarter of
+    // the flush of tile t-1's P bytes and the maximum of the previous block
+    // (whose MFMAs are two behind), each fixed in place so that the optimiser
+    // neither sinks the maxima past the MFMAs nor the flush into stage 2 ----
     __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* kt = cur ? Ks1 : Ks0;
+    auto kread = [&](int m, int c2) {
+      const uint8_t* kb = kt + kD * (64 * (m >> 1) + 16 * (m & 1));
+      return op8(ld16(kb + lk[2 * c2]), ld16(kb + lk[2 * c2 + 1]));
+    };
     v16f s[4];
+    float Mb[4];
+    v8i ka = kread(0, 0), kc = kread(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      v8i na = ka, nc = kc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[m][r] = 0.0f;
-      const uint8_t* kb = (cur ? Ks1 : Ks0) + kD * (64 * (m >> 1) + 16 * (m & 1));
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-        s[m] = mfma32(op8(ld16(kb + lk[2 * c2]), ld16(kb + lk[2 * c2 + 1])), qop[c2], s[m]);
+      s[m] = mfma32(ka, qop[0], s[m]);
+      if (m < 3) na = kread(m + 1, 0);
+      if (kPMode == VC_P_EXPCAST) {
+        flush_q(2 * m);
+        asm volatile("" : "+v"(pk[4 * m]), "+v"(pk[4 * m + 1]));
+      }
+      s[m] = mfma32(kc, qop[1], s[m]);
+      if (m < 3) nc = kread(m + 1, 1);
+      if (kPMode == VC_P_EXPCAST) {
+        flush_q(2 * m + 1);
+        asm volatile("" : "+v"(pk[4 * m + 2]), "+v"(pk[4 * m + 3]));
+      }
       if ((m & 1) == 0) copy_k(t + 1, cur ^ 1, m >> 1);
       else copy_v(t, cur, m >> 1);
+      if (m >= 1) {
+        Mb[m - 1] = s[m - 1][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) Mb[m - 1] = fmaxf(Mb[m - 1], s[m - 1][r]);
+        asm volatile("" : "+v"(Mb[m - 1]));
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // flush share
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA 2m
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads for MFMA 2m + 2
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // flush share
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA 2m + 1
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads for MFMA 2m + 3
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // tile copy
+      __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);   // block maximum
+      __builtin_amdgcn_sched_barrier(0);
+      ka = na;
+      kc = nc;
     }
-    if (kPMode == VC_P_EXPCAST) flush();
-    // the flushed bytes are materialised here, inside the Q.K region (the
-    // optimiser would otherwise sink the flush next to its use in stage 2)
+    {   // block 3 ends the Q.K MFMAs: a tree keeps its maximum's dependent chain short
+      float u[6];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(pk[i]));
-    // row max of the 32-key blocks, each once its two MFMAs are done (keys
-    // past N are taken out below, on the last tile only)
-    float Mb[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      Mb[m] = s[m][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) Mb[m] = fmaxf(Mb[m], s[m][r]);
+      for (int j = 0; j < 5; ++j) u[j] = fmaxf(fmaxf(s[3][3 * j], s[3][3 * j + 1]), s[3][3 * j + 2]);
+      u[5] = s[3][15];
+      Mb[3] = fmaxf(fmaxf(fmaxf(u[0], u[1]), u[2]), fmaxf(fmaxf(u[3], u[4]), u[5]));
     }
-    // issue order: the operand reads run two MFMAs ahead, so their latency
-    // passes under the VALU work (the flush, and the block maxima as their
-    // scores arrive) that follows each MFMA; a tile copy after every second MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // LDS reads of MFMAs 0, 1
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA i
-      __builtin_amdgcn_sched_group_barrier(0x002, kPMode == VC_P_EXPCAST ? 8 : 3, 0);   // VALU
-      if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads of MFMA i + 2
-      if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // tile copy
-    }
-    __builtin_amdgcn_sched_barrier(0);
     float M = fmaxf(fmaxf(Mb[0], Mb[1]), fmaxf(Mb[2], Mb[3]));
     if ((t + 1) * kBlock > N) {   // last tile: keys beyond N take no part
 #pragma unroll
@@ -462,9 +482,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     pv(std::integral_constant<int, cur ^ 1>{});
 #pragma unroll
     for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(pn[i]));
-    // issue order: operand reads two P.V MFMAs ahead; after each of the ten
-    // MFMAs (eight P.V, two row sums) a share of the P bytes of tile t
+    // issue order: operand reads two P.V MFMAs ahead; a share of the P bytes of
+    // tile t under the first reads' latency, then one after each of the ten
+    // MFMAs (eight P.V, two row sums)
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 13, 0);
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);

@@ -4,7 +4,9 @@
 // conversions, the accuracy of the hardware exp2); this entry point runs each
 // instruction alone so that tests can record those facts against exact
 // arithmetic on the host.  Three plain HBM streams (read only, copy, two reads
-// per write) measure the bandwidth the memory-bound passes can reach.
+// per write) measure the bandwidth the memory-bound passes can reach; two rate
+// kernels measure the FP8 matrix-instruction throughput and how fast one or two
+// wavefronts per SIMD issue vector instructions.
 #include "vc_common.h"
 
 namespace vc {
@@ -121,6 +123,46 @@ __global__ void __launch_bounds__(256) probe_mfma_rate(const uint8_t* __restrict
   out[blockIdx.x * 256 + tid] = sum;
 }
 
+// VALU issue rate (what = 9): n workgroups of 512 threads, one per CU (the
+// LDS array keeps a second one off), wavefront w on SIMD w % 4.  in[0] selects
+// the instruction (0: V_FMA_F32, 1: V_EXP_F32 of -|x|), in[1] the number of
+// wavefronts that run it (4: one per SIMD, 8: two); each runs kValuIters
+// iterations of eight independent chains.  out [n * 8][2] int64: per wavefront
+// the s_memtime ticks of its loop (0 for idle wavefronts) and the bits of its
+// lane-0 chain sum (so the chains are not optimised away).
+constexpr int kValuIters = 4096;
+__global__ void __launch_bounds__(512) probe_valu_rate(const int* __restrict__ cfg, long long* __restrict__ out) {
+  __shared__ float pad[24576];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int mode = cfg[0], active = cfg[1];
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.01f * (float)((tid + 3 * i) & 63) - 0.3f;
+  pad[tid] = x[0];
+  __syncthreads();
+  long long t0 = 0, t1 = 0;
+  if (wave < active) {
+    t0 = __builtin_amdgcn_s_memtime();
+    if (mode == 0) {
+      for (int it = 0; it < kValuIters; ++it)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], 0.999f, -0.25f);
+    } else {
+      for (int it = 0; it < kValuIters; ++it)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(-__builtin_fabsf(x[i]));
+    }
+    t1 = __builtin_amdgcn_s_memtime();
+  }
+  float sum = pad[(tid + 64) & 511];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += x[i];
+  if ((tid & 63) == 0) {
+    out[2 * (blockIdx.x * 8 + wave)] = t1 - t0;
+    out[2 * (blockIdx.x * 8 + wave) + 1] = (long long)__float_as_uint(sum);
+  }
+}
+
 }  // namespace vc
 
 using namespace vc;
@@ -141,6 +183,9 @@ extern "C" int vc_device_probe(int what, const void* in, void* out, int n, void*
       hipLaunchKernelGGL(probe_read2_write1, dim3(kStreamGrid), block, 0, st, (const uint4*)in, (uint4*)out, (long long)n);
       break;
     case 8: hipLaunchKernelGGL(probe_mfma_rate, dim3((unsigned)n), block, 0, st, (const uint8_t*)in, (float*)out); break;
+    case 9:
+      hipLaunchKernelGGL(probe_valu_rate, dim3((unsigned)n), dim3(512), 0, st, (const int*)in, (long long*)out);
+      break;
     default: return VC_ERR_UNSUPPORTED;
   }
   const hipError_t e = hipGetLastError();

@@ -278,6 +278,12 @@ int vc_attn_fwd_dump(const uint8_t* q_codes, const float* q_scales,
  *   what 8  n workgroups x 4 wavefronts, each 2048 x 4 independent
  *           V_MFMA_F32_32X32X64_F8F6F4 on operands from in (u8 [2048])
  *                                               -> out fp32 [n*256] (accumulator sums)
+ * and the vector-instruction issue rate:
+ *   what 9  n workgroups x 8 wavefronts (one workgroup per CU), in = i32 [2]
+ *           {instruction: 0 V_FMA_F32, 1 V_EXP_F32; wavefronts running it:
+ *           4 = one per SIMD, 8 = two}, each running wavefront 4096 x 8
+ *           independent chains   -> out i64 [n*8][2] (s_memtime ticks of the
+ *           loop, 0 when idle; bits of the lane-0 chain sum)
  * Returns VC_ERR_UNSUPPORTED for other `what`, VC_ERR_INVALID_ARG for null
  * pointers or n < 1.
  * ------------------------------------------------------------------------ */

@@ -11,7 +11,10 @@ vc_device_probe test hook against exact arithmetic on the host:
 - V_CVT_PK_U8_F32 rounds to nearest even and clamps to [0, 255] (the ExpCast
   code conversion);
 - V_EXP_F32 is within one ulp of exp2 (the conventional P path's codes may move
-  one step at rounding boundaries).
+  one step at rounding boundaries);
+- and, reported rather than asserted, how fast one or two wavefronts per SIMD
+  issue V_FMA_F32 and V_EXP_F32 (the reason the attention kernel keeps two
+  wavefronts of the same step on every SIMD).
 """
 import math
 import sys
@@ -227,3 +230,35 @@ def test_mfma_rate_probe_runs_and_is_deterministic(vc):
     torch.cuda.synchronize()
     assert torch.isfinite(out1).all()
     assert torch.equal(out1, out2)
+
+
+def valu_rates(vc, n=256):
+    """Per-SIMD issue rates (instructions per s_memtime tick) of V_FMA_F32 and
+    V_EXP_F32 with one and with two wavefronts per SIMD (the rate probe, one
+    workgroup per CU)."""
+    dev = torch.device("cuda:0")
+    out = torch.zeros(n * 8 * 2, dtype=torch.int64, device=dev)
+    rates = {}
+    for name, mode in (("fma", 0), ("exp", 1)):
+        for active in (4, 8):
+            cfg = torch.tensor([mode, active], dtype=torch.int32, device=dev)
+            vc.device_probe("valu_rate", cfg, out, n)
+            torch.cuda.synchronize()
+            r = out.view(n, 8, 2).cpu().numpy()
+            ticks = r[:, :, 0]
+            assert (ticks[:, :active] > 0).all() and (ticks[:, active:] == 0).all()
+            sums = r[:, :active, 1].astype(np.uint32).view(np.float32)
+            assert np.isfinite(sums).all()
+            per_simd = active // 4
+            rates[(name, per_simd)] = per_simd * 8 * 4096 / float(ticks[:, :active].mean())
+    return rates
+
+
+def test_valu_rate_probe(vc):
+    """The issue-rate kernel runs every requested wavefront (and only those),
+    and records how fast one or two wavefronts per SIMD issue V_FMA_F32 and
+    V_EXP_F32 (printed; the timing is reported, not asserted)."""
+    _say("device probe: VALU issue rate, 256 workgroups")
+    r = valu_rates(vc)
+    _say(f"  FMA issue rate, one wavefront per SIMD vs two: {r[('fma', 1)] / r[('fma', 2)]:.2f}; "
+         f"V_EXP_F32 cost vs V_FMA_F32 (two per SIMD): {r[('fma', 2)] / r[('exp', 2)]:.2f}")
