@@ -176,23 +176,27 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     else if (i == 0) dma16_buf(vrs, (buf ? Vs1 : Vs0) + 1024 * wave, dvoff, (uint32_t)t * kVTile);
     else if (wave == 0) dma16_buf(vgrs, (buf ? Vs1 : Vs0) + 8192, (uint32_t)lane * 16u, (uint32_t)t * 512u);
   };
-  auto store_means = [&](int t) {
-    if (tid < kD) {
-      const float mu = bf16_bits_to_f32(mr) * InvSv[tid];
-      const uint32_t hi = __float_as_uint(mu) & 0xFFFF0000u;
-      const uint32_t lo = f32_to_bf16_rne(mu - __uint_as_float(hi));
-      const int sl = t & 3;
-      uint2 w;
-      w.x = (hi >> 16) | (lo << 16);
-      w.y = hi >> 16;
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(MuB[(t >> 2) & 1]) +
-                                (((tid >> 5) * 2 + (sl >> 1)) * 32 + (tid & 31)) * 16 + 8 * (sl & 1)) = w;
-    }
+  // the block means of restore batch j (tiles 4j .. 4j+3): thread tid takes
+  // channel tid % 128 of tile 4j + tid / 128 (tiles past the last one reload it:
+  // their row sums are zero)
+  auto load_means = [&](int j) {
+    mr = mbase[(long long)min(4 * j + (tid >> 7), nb - 1) * kD + (tid & (kD - 1))];
+  };
+  auto store_means = [&](int j) {
+    const int c = tid & (kD - 1), sl = tid >> 7;
+    const float mu = bf16_bits_to_f32(mr) * InvSv[c];
+    const uint32_t hi = __float_as_uint(mu) & 0xFFFF0000u;
+    const uint32_t lo = f32_to_bf16_rne(mu - __uint_as_float(hi));
+    uint2 w;
+    w.x = (hi >> 16) | (lo << 16);
+    w.y = hi >> 16;
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(MuB[j & 1]) +
+                              (((c >> 5) * 2 + (sl >> 1)) * 32 + (c & 31)) * 16 + 8 * (sl & 1)) = w;
   };
 
   copy_k(0, 0, 0);
   copy_k(0, 0, 1);
-  if (tid < kD) mr = mbase[tid];
+  load_means(0);
   ksn = a.ks[(long long)bh * nb];
   float ksc = ksn;
   reinterpret_cast<uint4*>(&MuB[0][0])[tid] = make_uint4(0u, 0u, 0u, 0u);
@@ -339,8 +343,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
     constexpr int cur = slot & 1;   // buffers of K tile t and V tile t; V tile t-1 is in cur ^ 1
     {
       const int tn = min(t + 1, nb - 1);   // next block (the last step reloads its own, unused)
-      if (tid < kD) mr = mbase[(long long)tn * kD + tid];
       ksn = a.ks[(long long)bh * nb + tn];
+      // the means of the next restore batch: loaded in slot 0, paired in slot 2
+      // (after the restore of slot 1 has read the buffer they overwrite)
+      if (slot == 0) load_means((t >> 2) + 1);
     }
     // ---- the row sum of tile t-2 joins l ----
     take_rowsum((slot + 2) & 3);
@@ -506,7 +512,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fp8_e4m3(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) pk[i] = pn[i];
 
-    if (t + 1 < nb) store_means(t + 1);
+    if (slot == 2) store_means((t >> 2) + 1);
     wait_dma();
     __syncthreads();
     ksc = ksn;
