@@ -22,10 +22,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=o
 
 
 # per-source extra flags: the screened k-means keeps its MFMA accumulators in
-# VGPRs (no AGPR copies, one more wavefront per SIMD); the FP8 attention kernels
-# see no NaN (finite codes and scales, -inf only for keys past N), so their
-# maxima need not quiet NaN inputs first (one instruction per operand otherwise)
-EXTRA = {"vsmooth.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "attn_fp8.hip": ["-fno-honor-nans"]}
+# VGPRs (no AGPR copies, one more wavefront per SIMD); the attention kernels see
+# no NaN (finite codes, scales and bf16 inputs, -inf only for keys past N), so
+# their maxima need not quiet NaN inputs first (one instruction per operand
+# otherwise)
+EXTRA = {"vsmooth.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "attn_fp8.hip": ["-fno-honor-nans"],
+         "attn_bf16.hip": ["-fno-honor-nans"]}
 
 
 def sources():

@@ -11,8 +11,11 @@
 // query's scores and the bf16 P values are already in the B-operand layout of
 // O^T = V^T.P^T.  A first kernel writes V transposed per 128-key block into the
 // caller's workspace (one HBM pass); the attention kernel then streams K and V^T
-// tiles global -> LDS directly, double buffered, 8 wavefronts (256 queries) per
-// workgroup so that two wavefronts share each SIMD.
+// tiles global -> LDS directly through buffer resources, double buffered in
+// 128 KiB of static LDS, 8 wavefronts (256 queries) per workgroup so that two
+// wavefronts share each SIMD.  Operand reads address the LDS through per-lane
+// registers plus constants that fit the instruction's 16-bit offset, so no
+// address arithmetic sits beside the MFMAs.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -69,14 +72,28 @@ __global__ void __launch_bounds__(256) transpose_v_bf16(const uint16_t* __restri
   }
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// 32-bit LDS address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(size_t)(const lds_u8*)(p);
+}
+// 16 bytes from LDS address `addr` (a register base plus a constant that fits
+// the instruction's 16-bit offset)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_read16(uint32_t addr) {
+  const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((size_t)addr);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* Kt = smem;                 // [2][128 keys][256 B], swizzled chunks
-  uint8_t* Vt = smem + 2 * kTileB;    // [2][128 ch][256 B], swizzled chunks
+  __shared__ __align__(16) uint8_t Kt[2][kTileB];   // [128 keys][256 B], swizzled chunks
+  __shared__ __align__(16) uint8_t Vt[2][kTileB];   // [128 ch][256 B], swizzled chunks
 
   const int item = xcd_item(blockIdx.x, a.nqb * a.BH);
   const int bh = item / a.nqb, qb = item % a.nqb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: copy destinations stay scalar
   const int g = lane >> 5, col = lane & 31;
   const int N = a.N, nb = a.nb;
 
@@ -91,44 +108,49 @@ __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
       qop[j] = as_bf(u);
     }
   }
-  const uint16_t* kbase = a.k + (long long)bh * N * kD;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vt + (long long)bh * nb * kBlock * kD);
+  // copies through buffer resources: K rows past N (lane offsets past the
+  // head's N rows) read as zeros; V^T tiles are padded, their tile offset is scalar
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + (long long)bh * N * kD, (uint32_t)N * kRowB);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(a.vt + (long long)bh * nb * kBlock * kD, (uint32_t)nb * kTileB);
 
   // DMA: instruction j (32 per operand per tile, 4 per wave) fills LDS bytes
   // [1024j, 1024j+1024) = rows 4j..4j+3; lane i writes row 4j + i/16 at chunk
   // position i%16.
-  uint32_t dk_row[4], dk_pos[4], dvoff[4];
+  uint32_t dkoff[4], dvoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = 8 * i + wave;
     const int row = 4 * j + (lane >> 4), pos = lane & 15;
-    dk_row[i] = (uint32_t)row;
-    dk_pos[i] = (uint32_t)(8 * (pos ^ swz_kb(row)));            // element offset in the K row
+    dkoff[i] = (uint32_t)(row * kRowB + 16 * (pos ^ swz_kb(row)));
     dvoff[i] = (uint32_t)(row * kRowB + 16 * (pos ^ (row & 15)));
   }
   auto load_tile = [&](int t, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 8 * i + wave;
-      const int key = min(t * kBlock + (int)dk_row[i], N - 1);   // rows past N are masked later
-      dma16(kbase + (long long)key * kD + dk_pos[i], Kt + buf * kTileB + 1024 * j);
-      dma16(vbase + (long long)t * kTileB + dvoff[i], Vt + buf * kTileB + 1024 * j);
+      dma16_buf(krs, Kt[buf] + 1024 * j, (uint32_t)t * kTileB + dkoff[i], 0u);   // rows past N: zeros, masked later
+      dma16_buf(vrs, Vt[buf] + 1024 * j, dvoff[i], (uint32_t)t * kTileB);
     }
   };
   // LDS operand addresses (rows sigma(m, col) share the K swizzle, channels
   // 32*cb + col share the V^T swizzle)
+  // per-lane LDS addresses of the operand reads (K tile 0 and V^T tile 0),
+  // kept opaque so that every read is a register plus an in-range constant
+  // (buffer, 32-key block, channel block): the V^T tiles lie above 64 KiB
   uint32_t lk[8], lv[8];
   {
     const int kr = sigma(0, col), ksw = swz_kb(kr), vsw = col & 15;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lk[j] = (uint32_t)(kr * kRowB + 16 * ((2 * j + g) ^ ksw));
+    for (int j = 0; j < 8; ++j) lk[j] = lds_addr(Kt[0]) + (uint32_t)(kr * kRowB + 16 * ((2 * j + g) ^ ksw));
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int chunk = 8 * (m >> 1) + 4 * g + 2 * (m & 1) + s2;
-        lv[2 * m + s2] = (uint32_t)(col * kRowB + 16 * (chunk ^ vsw));
+        lv[2 * m + s2] = lds_addr(Vt[0]) + (uint32_t)(col * kRowB + 16 * (chunk ^ vsw));
       }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(lk[j]), "+v"(lv[j]));
   }
 
   load_tile(0, 0);
@@ -154,8 +176,6 @@ __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
 
   auto step = [&](const int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const uint8_t* K = Kt + buf * kTileB;
-    const uint8_t* V = Vt + buf * kTileB;
     if (t + 1 < nb) load_tile(t + 1, buf ^ 1);
 
     v16f s[4];
@@ -163,9 +183,9 @@ __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[m][r] = 0.0f;
-      const uint8_t* kb = K + kRowB * (64 * (m >> 1) + 16 * (m & 1));
+      const uint32_t kb = (uint32_t)(buf * kTileB + kRowB * (64 * (m >> 1) + 16 * (m & 1)));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s[m] = mfma_bf16(as_bf(*reinterpret_cast<const uint4*>(kb + lk[j])), qop[j], s[m]);
+      for (int j = 0; j < 8; ++j) s[m] = mfma_bf16(as_bf(lds_read16(lk[j] + kb)), qop[j], s[m]);
     }
     if ((t + 1) * kBlock > N) {
 #pragma unroll
@@ -213,7 +233,7 @@ __global__ void __launch_bounds__(kB16Threads, 1) attn_bf16_kernel(B16Args a) {
         const v8bf pop = as_bf(make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-          const uint4 vv = *reinterpret_cast<const uint4*>(V + kRowB * 32 * cb + lv[2 * m + s2]);
+          const uint4 vv = lds_read16(lv[2 * m + s2] + (uint32_t)(buf * kTileB + kRowB * 32 * cb));
           o[cb] = mfma_bf16(as_bf(vv), pop, o[cb]);
         }
         rs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop, rs, 0, 0, 0);
@@ -274,13 +294,7 @@ extern "C" int vc_attn_bf16_fwd(const uint16_t* Q, const uint16_t* K, const uint
   uint16_t* vt = static_cast<uint16_t*>(workspace);
   hipLaunchKernelGGL(transpose_v_bf16, dim3(nb, B * H), dim3(256), 0, st, V, N, nb, vt);
   B16Args a{Q, K, vt, out, N, nb, nqb, B * H, score_scale_c0(softmax_scale)};
-  const size_t lds = 4u * kTileB;   // 128 KiB: double-buffered K and V^T
-  // dynamic LDS above the default limit, set on every call: the attribute is per
-  // device, and a call may run on any device (cheap; no state kept)
-  const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_bf16_kernel),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (ea != hipSuccess) return vc_set_hip_error((int)ea);
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)(nqb * B * H)), dim3(kB16Threads), lds, st, a);
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)(nqb * B * H)), dim3(kB16Threads), 0, st, a);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? VC_OK : vc_set_hip_error((int)e);
 }
