@@ -288,6 +288,7 @@ extern "C" int vc_attn_bf16_fwd(const uint16_t* Q, const uint16_t* K, const uint
   const int nb = (N + kBlock - 1) / kBlock;
   const int nqb = (N + 255) / 256;
   if ((long long)nqb * B * H > 0x7FFFFFFFLL) return VC_ERR_INVALID_ARG;
+  if ((long long)nb * kTileB > 0xFFFFFFFFLL) return VC_ERR_INVALID_ARG;   // a head's K rows / V^T tiles in one buffer record
   const size_t need = vc_attn_bf16_workspace(B, H, N, d);
   if (!workspace || workspace_bytes < need) return VC_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);

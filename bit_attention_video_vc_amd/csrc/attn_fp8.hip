@@ -608,6 +608,7 @@ extern "C" int vc_attn_fp8_fwd(const uint8_t* q_codes, const float* q_scales, co
   if (B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
   const int nb = (N + kBlock - 1) / kBlock;
   if ((long long)nb * B * H > 0x7FFFFFFFLL) return VC_ERR_INVALID_ARG;
+  if ((long long)nb * kTile > 0xFFFFFFFFLL) return VC_ERR_INVALID_ARG;   // a head's codes in one buffer record
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float c0 = score_scale_c0(softmax_scale);
   if (v_format == VC_V_E4M3 && (p_mode == VC_P_EXPCAST || p_mode == VC_P_FP32EXP_E4M3)) {
@@ -641,6 +642,7 @@ extern "C" int vc_attn_fwd_dump(const uint8_t* q_codes, const float* q_scales, c
   if (B < 1 || H < 1 || N < 1) return VC_ERR_INVALID_ARG;
   const int nb = (N + kBlock - 1) / kBlock;
   if ((long long)nb * B * H > 0x7FFFFFFFLL) return VC_ERR_INVALID_ARG;
+  if ((long long)nb * kTile > 0xFFFFFFFFLL) return VC_ERR_INVALID_ARG;   // a head's codes in one buffer record
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float c0 = score_scale_c0(softmax_scale);
   const bool e4m3_p = p_mode == VC_P_EXPCAST || p_mode == VC_P_FP32EXP_E4M3;

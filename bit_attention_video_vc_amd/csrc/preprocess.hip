@@ -378,6 +378,7 @@ extern "C" int vc_preprocess_quant_ex(const uint16_t* Q, const uint16_t* K, cons
   if (Q && (!q_codes || !q_scales)) return VC_ERR_INVALID_ARG;
   if ((v_format == VC_V_NVFP4 || v_format == VC_V_MXFP4) && !v_group_scales) return VC_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || (long long)B * H > 65535) return VC_ERR_INVALID_ARG;
+  if ((long long)N * kD * 2 > 0xFFFFFFFFLL) return VC_ERR_INVALID_ARG;   // a head's V rows in one buffer record
   if (hadamard != 0 && hadamard != 1) return VC_ERR_INVALID_ARG;
   const size_t need = vc_preprocess_workspace(B, H, N, d, v_format);
   if (!workspace || workspace_bytes < need) return VC_ERR_WORKSPACE;

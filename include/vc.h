@@ -47,7 +47,8 @@ extern "C" {
 
 enum vc_status {
   VC_OK = 0,
-  VC_ERR_INVALID_ARG = -1, /* null required pointer, N < 1, B/H < 1, k out of [1,256], iters < 1 */
+  VC_ERR_INVALID_ARG = -1, /* null required pointer, N < 1, B/H < 1, k out of [1,256], iters < 1, or N
+                              past 16,777,215 where a head's bytes must fit a 32-bit buffer record count */
   VC_ERR_UNSUPPORTED = -2, /* d != 128, unknown p_mode / v_format, or a mode pairing not built */
   VC_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than the *_workspace() size */
   VC_ERR_HIP = -4,         /* a HIP launch failed; see vc_last_hip_error() */

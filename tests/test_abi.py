@@ -88,6 +88,10 @@ def test_argument_errors_are_synchronous(L):
     assert L.vc_attn_bf16_fwd(p, p, null, 1, 1, 8, 128, 0.1, p, p, 1 << 20, null) == -1
     assert L.vc_attn_bf16_fwd(p, p, p, 1, 1, 8, 128, 0.1, p, p, 16, null) == -3
     assert L.vc_attn_bf16_workspace(1, 2, 300, 128) == 2 * 3 * 128 * 256
+    # a head's bytes must fit one 32-bit buffer record count: longer sequences are refused
+    assert L.vc_attn_fp8_fwd(*[p] * 8, 1, 1, (1 << 25) + 1, 128, 0.1, 0, 0, p, null) == -1
+    assert L.vc_attn_bf16_fwd(p, p, p, 1, 1, 1 << 24, 128, 0.1, p, p, 1 << 40, null) == -1
+    assert L.vc_preprocess_quant(p, p, p, p, 1, 1, 1 << 24, 128, 0, *outs, p, 1 << 40, null) == -1
     assert L.vc_attn_fp8_fwd_dump(*[p] * 7, 1, 1, 8, 128, 0.1, 2, p, p, p, null) == -2
 
 
