@@ -240,6 +240,26 @@ def valu_issue_probe(vc):
             "exp_cost_vs_fma_two_wavefronts_per_simd": round(rate[(0, 2)] / rate[(1, 2)], 3)}
 
 
+def lds_copy_probe(vc, n=256, iters=2048):
+    """s_memtime ticks per 64-lane load per CU of the probe hook's copy-rate
+    kernel (one workgroup per CU): 16 and 4 bytes per lane into LDS, and 16 bytes
+    per lane into registers, with the 4-byte time as a fraction of the 16-byte
+    one (near 1 when a copy costs per instruction rather than per byte)."""
+    import torch
+    inp = torch.zeros(256 + 8192, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(n * 8 * 2, dtype=torch.int64, device="cuda")
+    ticks = {}
+    for mode in (0, 1, 2):
+        inp[:8].view(torch.int32).copy_(torch.tensor([mode, iters], dtype=torch.int32, device="cuda"))
+        vc.device_probe("lds_copy_rate", inp, out, n)
+        torch.cuda.synchronize()
+        ticks[mode] = out.view(n, 8, 2)[:, :, 0].double().mean().item() / (64 * iters)
+    return {"ticks_per_copy_16B_lanes_to_lds": round(ticks[0], 3),
+            "ticks_per_copy_4B_lanes_to_lds": round(ticks[1], 3),
+            "ticks_per_load_16B_lanes_to_registers": round(ticks[2], 3),
+            "copy_4B_vs_16B_time": round(ticks[1] / ticks[0], 3)}
+
+
 def timed(fn, reps, stream):
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
@@ -437,6 +457,7 @@ def main():
     del prep5, out5
     mfma_peak = mfma_probe_tflops(vc, stream)
     valu_probe = valu_issue_probe(vc)
+    copy_probe = lds_copy_probe(vc)
     ms_bf16 = timed(lambda: vc.attn_bf16_fwd(Qd, Kd, Vd, scale, out=out), 3, stream)
     ms_sdpa = library_sdpa_ms(Qd, Kd, Vd)
     streams = hbm_streams(vc, stream)
@@ -488,6 +509,7 @@ def main():
                              "tflops": round(4.0 * N * N * 128 * H5 * B / (ms5 * 1e-3) / 1e12, 1)},
         "mfma_fp8_probe_tflops": mfma_peak,
         "valu_issue_probe": valu_probe,
+        "lds_copy_probe": copy_probe,
         "sclk_mhz_during_attention": clk.mean(),
         "p_path_ablation": ablation,
         "bf16_comparator": {"ms": round(ms_bf16, 3), "tflops": round(flops / (ms_bf16 * 1e-3) / 1e12, 1),

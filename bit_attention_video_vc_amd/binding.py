@@ -219,7 +219,7 @@ def attn_fwd_dump(prep: dict, softmax_scale: float | None = None, p_mode="expcas
 
 _PROBES = {"cvt_fp8": 0, "cvt_u8": 1, "exp2": 2, "mfma_32x32x64": 3, "mfma_16x16x128": 4,
            "hbm_read": 5, "hbm_copy": 6, "hbm_read2_write1": 7, "mfma_fp8_rate": 8,
-           "valu_rate": 9}
+           "valu_rate": 9, "lds_copy_rate": 10}
 
 
 def device_probe(what: str, inp: torch.Tensor, out: torch.Tensor, n: int):

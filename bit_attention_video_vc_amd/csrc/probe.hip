@@ -4,10 +4,11 @@
 // conversions, the accuracy of the hardware exp2); this entry point runs each
 // instruction alone so that tests can record those facts against exact
 // arithmetic on the host.  Three plain HBM streams (read only, copy, two reads
-// per write) measure the bandwidth the memory-bound passes can reach; two rate
-// kernels measure the FP8 matrix-instruction throughput and how fast one or two
-// wavefronts per SIMD issue vector instructions.
-#include "vc_common.h"
+// per write) measure the bandwidth the memory-bound passes can reach; three rate
+// kernels measure the FP8 matrix-instruction throughput, how fast one or two
+// wavefronts per SIMD issue vector instructions, and how fast a CU issues the
+// global -> LDS copies that stage the attention tiles.
+#include "attn_common.h"
 
 namespace vc {
 
@@ -163,6 +164,64 @@ __global__ void __launch_bounds__(512) probe_valu_rate(const int* __restrict__ c
   }
 }
 
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+
+// Global -> LDS copy rate (what = 10): n workgroups of 512 threads, one per CU
+// (the LDS array keeps a second one off).  `in` holds i32 {mode, iterations} in
+// its first 256 bytes and an 8 KiB source after them, which every wavefront
+// reads again and again (it stays in the caches).  Each iteration a wavefront
+// issues eight 64-lane loads through a buffer resource and then waits for them:
+// mode 0 `buffer_load_dwordx4 ... lds` (16 bytes per lane into LDS), mode 1
+// `buffer_load_dword ... lds` (4 bytes per lane into LDS), mode 2
+// `buffer_load_dwordx4` into registers (XORed into a checksum).  out [n * 8][2]
+// int64: per wavefront the s_memtime ticks of its loop and a checksum that keeps
+// the loads alive.
+__global__ void __launch_bounds__(512) probe_lds_copy(const uint8_t* __restrict__ in, long long* __restrict__ out) {
+  __shared__ __align__(16) uint8_t buf[98304];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int mode = reinterpret_cast<const int*>(in)[0];
+  const int iters = reinterpret_cast<const int*>(in)[1];
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(in + 256, 8192u);   // lane offsets below stay under 8 KiB
+  uint8_t* dst = buf + 8192 * wave;                               // eight 1 KiB slots per wavefront
+  reinterpret_cast<uint4*>(buf)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  uint32_t acc = 0u;
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  if (mode == 0) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dma16_buf(rs, dst + 1024 * j, (uint32_t)(16 * lane + 1024 * j), 0u);
+      wait_dma();
+    }
+  } else if (mode == 1) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 4,
+                                                 4 * lane + 256 * j, 0, 0, 0);
+      wait_dma();
+    }
+  } else {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // the lane offset moves with the iteration (inside the same 1 KiB), so the
+        // loads cannot be hoisted out of the loop
+        const uint32_t off = (uint32_t)(1024 * j + ((16 * lane) ^ (16 * (it & 63))));
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0u, 0);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      }
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  __syncthreads();
+  acc ^= reinterpret_cast<const uint32_t*>(buf)[(tid * 37) & 24575];
+  if (lane == 0) {
+    out[2 * (blockIdx.x * 8 + wave)] = t1 - t0;
+    out[2 * (blockIdx.x * 8 + wave) + 1] = (long long)acc;
+  }
+}
+
 }  // namespace vc
 
 using namespace vc;
@@ -185,6 +244,9 @@ extern "C" int vc_device_probe(int what, const void* in, void* out, int n, void*
     case 8: hipLaunchKernelGGL(probe_mfma_rate, dim3((unsigned)n), block, 0, st, (const uint8_t*)in, (float*)out); break;
     case 9:
       hipLaunchKernelGGL(probe_valu_rate, dim3((unsigned)n), dim3(512), 0, st, (const int*)in, (long long*)out);
+      break;
+    case 10:
+      hipLaunchKernelGGL(probe_lds_copy, dim3((unsigned)n), dim3(512), 0, st, (const uint8_t*)in, (long long*)out);
       break;
     default: return VC_ERR_UNSUPPORTED;
   }

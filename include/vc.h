@@ -285,6 +285,14 @@ int vc_attn_fwd_dump(const uint8_t* q_codes, const float* q_scales,
  *           4 = one per SIMD, 8 = two}, each running wavefront 4096 x 8
  *           independent chains   -> out i64 [n*8][2] (s_memtime ticks of the
  *           loop, 0 when idle; bits of the lane-0 chain sum)
+ * and the rate of the global -> LDS tile copies:
+ *   what 10 n workgroups x 8 wavefronts (one workgroup per CU), in = u8
+ *           [256 + 8192]: i32 {mode, iterations} then an 8 KiB source; each
+ *           iteration a wavefront issues eight 64-lane loads of the source and
+ *           waits: mode 0 16 bytes per lane into LDS, 1 4 bytes per lane into
+ *           LDS, 2 16 bytes per lane into registers
+ *                                               -> out i64 [n*8][2] (s_memtime ticks of the
+ *           loop; a checksum of the loaded data)
  * Returns VC_ERR_UNSUPPORTED for other `what`, VC_ERR_INVALID_ARG for null
  * pointers or n < 1.
  * ------------------------------------------------------------------------ */

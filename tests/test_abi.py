@@ -106,7 +106,7 @@ def test_test_hooks_reject_bad_arguments(L):
     assert L.vc_attn_fwd_dump(*a6, 0, 2, p, p, p, null) == -1         # MXFP4 needs its group scales
     assert L.vc_attn_fwd_dump(*a6, 2, 1, p, p, p, null) == -1         # so does NVFP4
     assert L.vc_attn_fwd_dump(*[p] * 8, 1, 1, 8, 64, 0.1, 0, 0, p, p, p, null) == -2
-    assert L.vc_device_probe(10, p, p, 4, null) == -2
+    assert L.vc_device_probe(11, p, p, 4, null) == -2
     assert L.vc_device_probe(0, p, p, 0, null) == -1
     assert L.vc_device_probe(0, null, p, 4, null) == -1
 

@@ -262,3 +262,34 @@ def test_valu_rate_probe(vc):
     r = valu_rates(vc)
     _say(f"  FMA issue rate, one wavefront per SIMD vs two: {r[('fma', 1)] / r[('fma', 2)]:.2f}; "
          f"V_EXP_F32 cost vs V_FMA_F32 (two per SIMD): {r[('fma', 2)] / r[('exp', 2)]:.2f}")
+
+
+def lds_copy_ticks(vc, n=256, iters=2048):
+    """s_memtime ticks per 64-lane load per CU of the copy-rate kernel (one
+    workgroup per CU, eight wavefronts, each issuing eight loads per iteration
+    and waiting): mode 0 16 bytes per lane into LDS, 1 4 bytes per lane into
+    LDS, 2 16 bytes per lane into registers."""
+    dev = torch.device("cuda:0")
+    inp = torch.zeros(256 + 8192, dtype=torch.uint8, device=dev)
+    inp[256:] = torch.arange(8192, dtype=torch.int64, device=dev).remainder(251).to(torch.uint8)
+    out = torch.zeros(n * 8 * 2, dtype=torch.int64, device=dev)
+    ticks = {}
+    for mode in (0, 1, 2):
+        inp[:8].view(torch.int32).copy_(torch.tensor([mode, iters], dtype=torch.int32, device=dev))
+        vc.device_probe("lds_copy_rate", inp, out, n)
+        torch.cuda.synchronize()
+        t = out.view(n, 8, 2)[:, :, 0].cpu().numpy()
+        assert (t > 0).all()
+        ticks[mode] = float(t.mean()) / (64 * iters)
+    return ticks
+
+
+def test_lds_copy_rate_probe(vc):
+    """The copy-rate kernel runs every wavefront to the end in all three modes,
+    and records what a 64-lane global -> LDS copy costs a CU with 16 and with 4
+    bytes per lane, and a 16-byte load into registers (printed; the timing is
+    reported, not asserted)."""
+    _say("device probe: global -> LDS copy rate, 256 workgroups")
+    t = lds_copy_ticks(vc)
+    _say(f"  ticks per 64-lane copy per CU: 16 B/lane into LDS {t[0]:.2f}, 4 B/lane into LDS {t[1]:.2f}, "
+         f"16 B/lane into registers {t[2]:.2f}")
