@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(512) probe_lds_copy(const uint8_t* __restrict_
   const int iters = reinterpret_cast<const int*>(in)[1];
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(in + 256, 8192u);   // lane offsets below stay under 8 KiB
   uint8_t* dst = buf + 8192 * wave;                               // eight 1 KiB slots per wavefront
-  reinterpret_cast<uint4*>(buf)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < 98304 / 16; i += 512) reinterpret_cast<uint4*>(buf)[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   uint32_t acc = 0u;
   const long long t0 = __builtin_amdgcn_s_memtime();
@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(512) probe_lds_copy(const uint8_t* __restrict_
   }
   const long long t1 = __builtin_amdgcn_s_memtime();
   __syncthreads();
-  acc ^= reinterpret_cast<const uint32_t*>(buf)[(tid * 37) & 24575];
+  acc ^= reinterpret_cast<const uint32_t*>(buf)[(tid * 37) & 16383];   // inside the copied 64 KiB
   if (lane == 0) {
     out[2 * (blockIdx.x * 8 + wave)] = t1 - t0;
     out[2 * (blockIdx.x * 8 + wave) + 1] = (long long)acc;
