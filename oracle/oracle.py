@@ -21,9 +21,10 @@ E2M1, bfloat16.  Contractions whose result is exact in float64 use numpy's
 matmul as a step.  Where the pages leave the arithmetic open the reading taken is
 stated in the function's docstring.
 
-Parity status: every function here is pinned by a `-m "not gpu"` test, except
-the NVFP4 attention output (4-bit path), which is "parity unpinned" beyond its
-encoders (no page gives a number for it).
+Parity status: every function here is pinned by a `-m "not gpu"` test.  No page
+gives a number for the NVFP4 attention output (4-bit path); it is pinned by
+closed forms (uniform scores average the value tokens rebuilt from the stored
+codes; one dominant key returns its own rebuilt token).
 """
 from __future__ import annotations
 

@@ -179,3 +179,31 @@ def test_unscaled_scores_fail_the_brute_force_pin(monkeypatch):
     monkeypatch.setattr(O, "exact_attention", unscaled)
     with pytest.raises(AssertionError):
         TQ.test_exact_attention_matches_explicit_loops(7, 2)
+
+
+def test_nvfp4_values_with_the_next_groups_scale_fail_the_4bit_pins(monkeypatch):
+    from tests import test_oracle_nvfp4_attention as TN
+    real = O._nvfp4_encode
+
+    def shifted(R, N):
+        out = real(R, N)
+        sg = np.roll(out["v_group_scales"], 1, axis=0)          # each group decoded with its neighbour's scale
+        res = O.e2m1_decode(out["v_nibbles"][:N]) * O.e4m3_decode(np.repeat(sg, 16, axis=0)[:N])
+        out["v_res"] = res * np.float64(out["v_scales"][0])
+        return out
+
+    monkeypatch.setattr(O, "_nvfp4_encode", shifted)
+    with pytest.raises(AssertionError):
+        TN.test_uniform_scores_average_the_rebuilt_values()
+
+
+def test_dropped_mean_restore_fails_the_4bit_dominant_key_pin(monkeypatch):
+    from tests import test_oracle_nvfp4_attention as TN
+    real = O.online_attention
+
+    def no_restore(Qd, Kd, Vres, means, *a, **k):
+        return real(Qd, Kd, Vres, np.zeros_like(means), *a, **k)
+
+    monkeypatch.setattr(O, "online_attention", no_restore)
+    with pytest.raises(AssertionError):
+        TN.test_one_dominant_key_returns_its_rebuilt_value()
