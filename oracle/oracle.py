@@ -22,9 +22,9 @@ matmul as a step.  Where the pages leave the arithmetic open the reading taken i
 stated in the function's docstring.
 
 Parity status: every function here is pinned by a `-m "not gpu"` test.  No page
-gives a number for the NVFP4 attention output (4-bit path); it is pinned by
-closed forms (uniform scores average the value tokens rebuilt from the stored
-codes; one dominant key returns its own rebuilt token).
+gives a number for the 4-bit attention outputs (NVFP4 and MXFP4 residuals); they
+are pinned by closed forms (uniform scores average the value tokens rebuilt
+from the stored codes; one dominant key returns its own rebuilt token).
 """
 from __future__ import annotations
 

@@ -182,7 +182,7 @@ def test_unscaled_scores_fail_the_brute_force_pin(monkeypatch):
 
 
 def test_nvfp4_values_with_the_next_groups_scale_fail_the_4bit_pins(monkeypatch):
-    from tests import test_oracle_nvfp4_attention as TN
+    from tests import test_oracle_4bit_attention as TN
     real = O._nvfp4_encode
 
     def shifted(R, N):
@@ -194,11 +194,11 @@ def test_nvfp4_values_with_the_next_groups_scale_fail_the_4bit_pins(monkeypatch)
 
     monkeypatch.setattr(O, "_nvfp4_encode", shifted)
     with pytest.raises(AssertionError):
-        TN.test_uniform_scores_average_the_rebuilt_values()
+        TN.test_uniform_scores_average_the_rebuilt_values("nvfp4", "fp32_bf16")
 
 
 def test_dropped_mean_restore_fails_the_4bit_dominant_key_pin(monkeypatch):
-    from tests import test_oracle_nvfp4_attention as TN
+    from tests import test_oracle_4bit_attention as TN
     real = O.online_attention
 
     def no_restore(Qd, Kd, Vres, means, *a, **k):
@@ -206,4 +206,11 @@ def test_dropped_mean_restore_fails_the_4bit_dominant_key_pin(monkeypatch):
 
     monkeypatch.setattr(O, "online_attention", no_restore)
     with pytest.raises(AssertionError):
-        TN.test_one_dominant_key_returns_its_rebuilt_value()
+        TN.test_one_dominant_key_returns_its_rebuilt_value("nvfp4", "fp32_bf16")
+
+
+def test_mxfp4_groups_of_consecutive_rows_fail_the_4bit_pins(monkeypatch):
+    from tests import test_oracle_4bit_attention as TN
+    monkeypatch.setattr(O, "mxfp4_groups", lambda Np: np.arange(Np) // 32)   # 32 consecutive rows per group
+    with pytest.raises(AssertionError):
+        TN.test_uniform_scores_average_the_rebuilt_values("mxfp4", "expcast")
