@@ -451,3 +451,35 @@ def test_preprocess_quant_entry_point_itself(vc):
     assert set(direct) == {"q_codes", "q_scales", "k_codes", "k_scales", "v_codes", "v_scales", "v_means"}
     for k, v in direct.items():
         assert torch.equal(v, prep_ex[k]), k
+
+
+@pytest.mark.parametrize("case", ["uniform", "dominant"])
+@pytest.mark.parametrize("fmt,p_mode", [("e4m3", "expcast"), ("e4m3", "fp32exp_e4m3"), ("mxfp4", "expcast"),
+                                        ("mxfp4", "fp32exp_e4m3"), ("nvfp4", "fp32_bf16")])
+def test_closed_form_score_patterns(vc, fmt, p_mode, case):
+    """Two score patterns whose outputs have closed forms (the oracle is pinned
+    to them on the CPU): Q = 0, so every P is exactly 1 and each row is the mean
+    of the value tokens; and one key about 2^16 log2 units above every other,
+    so each row is that key's token and every tile before it is rescaled by 0.
+    Scores are exact in both (all partial sums are small multiples of one
+    product), so the kernel meets the oracle within the given-S bar."""
+    _say(f"closed-form scores ({case}): B1 H1 N300, {fmt} / {p_mode}")
+    N = 300
+    _, _, V = W.custom_inputs(1, 1, N, seed=91, recipe="clustered")
+    if case == "uniform":
+        Q = torch.zeros(1, 1, N, 128, dtype=torch.bfloat16)
+        K = W.custom_inputs(1, 1, N, seed=92, recipe="clustered")[1]
+    else:
+        Q = torch.full((1, 1, N, 128), 64.0, dtype=torch.bfloat16)
+        K = torch.zeros(1, 1, N, 128, dtype=torch.bfloat16)
+        K[0, 0, 137] = 64.0
+    dev = torch.device("cuda:0")
+    perm_np = np.random.default_rng(93).permutation(N).astype(np.int32)
+    perm = torch.from_numpy(perm_np).to(dev).reshape(1, 1, N)
+    prep = vc.preprocess_quant(Q.to(dev), K.to(dev), V.to(dev), perm, fmt)
+    out = vc.attn_fp8_fwd(prep, SCALE, p_mode).cpu().numpy()[0, 0]
+    pr = O.preprocess_head(_u16(Q[0, 0]), _u16(K[0, 0]), _u16(V[0, 0]), perm_np, fmt)
+    want = O.vc_attention_head(pr, SCALE, p_mode)
+    e = O.rel_l2(out, want)
+    _say(f"  output rel-L2 vs oracle {e:.2e}")
+    assert np.isfinite(out).all() and e <= TOL_GIVEN_S
